@@ -1,0 +1,176 @@
+"""Benchmark of the hot path on one MI355X.
+
+One step = one full pass over a batch of synthetic input: x_T for every map,
+the workload's guided DDIM steps (with seam projection for chains) and
+classical MDS of every final map.  Default workload: the genome-wide slab,
+2658 regions x 2 guidance weights x 100 trajectories = 531,600 maps (4.3 GB of
+float32 state), 50 steps, eta = 1.
+
+Prints one JSON line.  `value` is trajectory-steps per second of the whole
+pass; `roofline` describes the DDIM step kernel (HBM-bound), timed with HIP
+events on the stream it runs on; `cpu_baseline` times the float64 oracle on a
+bounded sample of the same workload on the host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+STEP_BYTES_PER_MAP = 2016 * 4 * 2   # read + write of one packed map per DDIM step
+REF_BYTES_PER_REGION = 2016 * 4 * 2  # conditional + unconditional reference, once per region per step
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=5, help="timed passes")
+    p.add_argument("--warmup", type=int, default=1, help="untimed passes")
+    p.add_argument("--workload", default="genome_slab")
+    p.add_argument("--n-steps", type=int, default=0, help="DDIM steps (default: the workload's first)")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target duration of the oracle baseline")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def cpu_baseline(wl, n_steps, seed, target_s):
+    """Time the oracle (as it stands) on a bounded sample of the workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import mds, sampler
+    from workloads import reference_maps
+
+    G, S = wl.n_guidance, wl.n_traj
+
+    def run(n_maps):
+        if wl.chain_len == 1:
+            idx = np.arange(n_maps)
+            r = idx // (G * S)
+            x0c, x0u = reference_maps(wl, seed, regions=sorted(set(r.tolist())))
+            pos = {v: k for k, v in enumerate(sorted(set(r.tolist())))}
+            rr = np.array([pos[v] for v in r])
+            w = np.asarray(wl.w)[(idx // S) % G]
+            t0 = time.perf_counter()
+            fin, _ = sampler.run_independent(x0c[rr], x0u[rr], w, idx, seed, n_steps, wl.eta)
+            t1 = time.perf_counter()
+        else:
+            x0c, x0u = reference_maps(wl, seed)
+            L = wl.chain_len
+            cols = max(1, n_maps // L)
+            tids = np.array([[(k * G + 0) * S + s for s in range(cols)] for k in range(L)])
+            w = np.full(cols, wl.w[0])
+            t0 = time.perf_counter()
+            fin, _, _, _ = sampler.run_chain(x0c[:L], x0u[:L], w, tids, seed, n_steps, wl.eta, wl.overlap)
+            t1 = time.perf_counter()
+            fin = fin.reshape(-1, 2016)
+            n_maps = fin.shape[0]
+        for m in fin:
+            mds.classical_mds(m)
+        t2 = time.perf_counter()
+        return n_maps, t1 - t0, t2 - t1
+
+    with threadpool_limits(limits=1):
+        n = 16
+        n_maps, ts, tm = run(n)
+        while ts + tm < target_s / 4 and n < wl.n_maps:
+            n = min(wl.n_maps, n * 4)
+            n_maps, ts, tm = run(n)
+    return {"value": n_maps * n_steps / (ts + tm), "unit": "trajectory-steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_maps} of {wl.n_maps} maps ({wl.name}), {n_steps} float64 DDIM steps + LAPACK MDS, "
+                      f"one thread; {ts:.1f} s sampling + {tm:.1f} s MDS",
+            "mds_maps_per_s": n_maps / tm, "step_traj_steps_per_s": n_maps * n_steps / ts,
+            "host_cpu_count": os.cpu_count(), "host_affinity": len(os.sched_getaffinity(0))}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the workloads need no inter-GPU communication and this build runs "
+              "on a single MI355X; --gpus N > 1 is not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import tiled_genome_diffusion_amd as pc
+    from workloads import get, reference_maps
+
+    wl = get(args.workload)
+    n_steps = args.n_steps or wl.n_steps[0]
+    dev = torch.device("cuda:0")
+    lay = pc.PCLayout(wl.n_regions, wl.n_guidance, wl.n_traj, wl.chain_len, wl.overlap if wl.chain_len > 1 else 0)
+    x0c, x0u = reference_maps(wl, args.seed)
+    x0c_d, x0u_d = torch.from_numpy(x0c).to(dev), torch.from_numpy(x0u).to(dev)
+    state = torch.empty(lay.n_maps * pc.PACKED, dtype=torch.float32, device=dev)
+    coords = torch.empty(lay.n_maps * 64 * 3, dtype=torch.float32, device=dev)
+    project = 1 if wl.chain_len > 1 else 0
+    stream = torch.cuda.current_stream(dev)
+
+    def one_pass(events=None):
+        pc.pc_init_state(state, lay, args.seed)
+        if events:
+            events[0].record(stream)
+        pc.pc_ddim_sample(state, x0c_d, x0u_d, list(wl.w), lay, n_steps, wl.eta, args.seed,
+                          project_every=project, init=False)
+        if events:
+            events[1].record(stream)
+        pc.pc_mds_recover(state, coords)
+        if events:
+            events[2].record(stream)
+
+    for _ in range(args.warmup):
+        one_pass()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        one_pass(evs[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_per_pass = (t1 - t0) * 1e3 / args.steps
+    step_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    mds_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    launch_ms = step_ms / n_steps
+    bytes_per_launch = lay.n_maps * STEP_BYTES_PER_MAP + lay.n_regions * REF_BYTES_PER_REGION
+    achieved = bytes_per_launch / (launch_ms * 1e-3) / 1e9
+    traj_steps = lay.n_maps * n_steps
+
+    out = {
+        "metric": "DDIM trajectory-steps/s (64-bead maps) + % HBM peak; MDS maps/s",
+        "value": traj_steps / (ms_per_pass * 1e-3),
+        "unit": "trajectory-steps/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_pass,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "maps": lay.n_maps, "regions": wl.n_regions, "guidance": wl.n_guidance,
+                   "trajectories": wl.n_traj, "chain_len": wl.chain_len, "ddim_steps": n_steps, "eta": wl.eta,
+                   "seed": args.seed, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "k_step_indep" if wl.chain_len == 1 else "k_step_chain",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None, "launch_us": launch_ms * 1e3, "bytes_per_launch": bytes_per_launch},
+        "step_loop_traj_steps_per_s": traj_steps / (step_ms * 1e-3),
+        "mds_maps_per_s": lay.n_maps / (mds_ms * 1e-3),
+        "mds_ms": mds_ms,
+        "step_loop_ms": step_ms,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, n_steps, args.seed, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -25,7 +25,7 @@ import math
 
 import numpy as np
 
-from .layout import idx, unpack
+from .layout import pair_table, unpack
 
 
 def double_centre(d) -> np.ndarray:
@@ -105,12 +105,9 @@ def classical_mds(packed, n: int = 64, solver: str = "eigh"):
 def coords_distances(coords) -> np.ndarray:
     """Packed pairwise distances [n(n-1)/2] of coordinates [n, d]."""
     x = np.asarray(coords, dtype=np.float64)
-    n = x.shape[0]
-    out = np.empty(n * (n - 1) // 2)
-    for i in range(n):
-        for j in range(i + 1, n):
-            out[idx(i, j, n)] = math.sqrt(float(np.sum((x[i] - x[j]) ** 2)))
-    return out
+    rows, cols = pair_table(x.shape[0])
+    diff = x[rows] - x[cols]
+    return np.sqrt(np.sum(diff * diff, axis=1))
 
 
 def procrustes(x, y):

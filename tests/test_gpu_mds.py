@@ -1,0 +1,92 @@
+"""GPU parity of batched classical MDS."""
+
+import numpy as np
+import pytest
+
+import tiled_genome_diffusion_amd as pc
+from gpu_util import DIST_RTOL, layout_of, run_steps, say, torch_dev, upload_refs
+from oracle import mds
+from workloads import get, packed_distances, random_walk, walk_rng
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_mds(maps_np, max_iters=0):
+    torch, dev = torch_dev()
+    maps = torch.from_numpy(np.ascontiguousarray(maps_np, dtype=np.float32)).to(dev)
+    n = maps_np.shape[0]
+    coords = torch.empty(n * 64 * 3, dtype=torch.float32, device=dev)
+    eig = torch.empty(n * 3, dtype=torch.float32, device=dev)
+    pc.pc_mds_recover(maps, coords, eig, max_iters)
+    return coords.cpu().numpy().reshape(n, 64, 3), eig.cpu().numpy().reshape(n, 3)
+
+
+def dist_err(coords, maps_oracle_coords):
+    """Per-map max |D_gpu - D_oracle| / max D_oracle, worst over maps."""
+    worst = 0.0
+    for c, o in zip(coords, maps_oracle_coords):
+        dg = mds.coords_distances(c)
+        do = mds.coords_distances(o)
+        worst = max(worst, float(np.abs(dg - do).max() / do.max()))
+    return worst
+
+
+def test_exact_walk_maps():
+    say("mds on exact walk maps")
+    walks = [random_walk(64, walk_rng(7, k), None if k % 2 else 0.25) for k in range(64)]
+    maps = np.array([packed_distances(w) for w in walks], dtype=np.float32)
+    coords, eig = gpu_mds(maps)
+    oc = [mds.classical_mds(m.astype(np.float64))[0] for m in maps]
+    assert dist_err(coords, oc) <= DIST_RTOL
+    for c, w in zip(coords, walks):
+        _, resid = mds.procrustes(c.astype(np.float64), w)
+        assert resid <= 1e-4 * np.abs(w - w.mean(axis=0)).max()
+    for c in coords:   # sign convention
+        for k in range(3):
+            assert c[np.argmax(np.abs(c[:, k])), k] > 0
+
+
+def test_closed_form_shapes():
+    say("mds closed forms")
+    line = np.stack([np.arange(64.0), np.zeros(64), np.zeros(64)], 1)
+    ang = 2 * np.pi * np.arange(64) / 64
+    ring = np.stack([3.5 * np.cos(ang), 3.5 * np.sin(ang), np.zeros(64)], 1)
+    maps = np.array([packed_distances(line), packed_distances(ring), np.zeros(2016)], dtype=np.float32)
+    coords, eig = gpu_mds(maps)
+    assert eig[0, 0] == pytest.approx(21840.0, rel=1e-5)
+    assert abs(eig[0, 1]) < 1e-2 and abs(eig[0, 2]) < 1e-2
+    assert eig[1, 0] == pytest.approx(64 * 3.5 ** 2 / 2, rel=1e-5)
+    assert eig[1, 1] == pytest.approx(64 * 3.5 ** 2 / 2, rel=1e-5)
+    for k, pts in ((0, line), (1, ring)):
+        d = mds.coords_distances(coords[k])
+        assert np.abs(d - packed_distances(pts)).max() <= DIST_RTOL * packed_distances(pts).max()
+    assert np.all(coords[2] == 0.0) and np.all(eig[2] == 0.0)   # all-zero map
+
+
+def test_final_maps_of_the_sampler():
+    wl = get("region_ensemble")
+    say("mds on the 2000 final maps of region_ensemble")
+    torch, dev = torch_dev()
+    refs = upload_refs(wl, 2)
+    _, state, _ = run_steps(wl, 2, 50, [0], set(), refs=refs)
+    final = state.view(wl.n_maps, 2016).cpu().numpy()
+    coords, _ = gpu_mds(final)
+    oc = [mds.classical_mds(m.astype(np.float64))[0] for m in final]
+    assert dist_err(coords, oc) <= DIST_RTOL
+
+
+def test_non_euclidean_maps():
+    # guided mixtures (w = 0.5) of two walk maps are not Euclidean: B has negative eigenvalues.
+    # Noisy walk maps: relative noise 1e-3.
+    say("mds on non-Euclidean maps")
+    rng = np.random.default_rng(3)
+    maps = []
+    for k in range(48):
+        a = packed_distances(random_walk(64, walk_rng(11, k, 0), None))
+        b = packed_distances(random_walk(64, walk_rng(11, k, 1), None))
+        maps.append(0.5 * (a + b) if k % 2 == 0 else a * (1 + 1e-3 * rng.standard_normal(2016)))
+    maps = np.array(maps, dtype=np.float32)
+    coords, eig = gpu_mds(maps, max_iters=256)
+    oc, ol = zip(*[mds.classical_mds(m.astype(np.float64)) for m in maps])
+    assert dist_err(coords, oc) <= DIST_RTOL
+    assert np.allclose(eig, np.array(ol), rtol=1e-4, atol=1e-4 * np.abs(np.array(ol)).max())

@@ -1,0 +1,136 @@
+// Shared definitions of the gfx950 kernels: map layout, Philox4x32-10,
+// Box-Muller, and the workgroup -> XCD remapping.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pc {
+
+constexpr int kBeads = 64;
+constexpr int kPacked = 2016;           // 64 * 63 / 2 distances per map
+constexpr int kQuads = kPacked / 4;     // 504 float4 per map; one Philox block each
+constexpr int kMaxGuidance = 16;
+constexpr int kMaxOverlap = 32;
+constexpr int kMaxPairs = kMaxOverlap * (kMaxOverlap - 1) / 2;
+
+// Packed index of bead pair (i, j), i < j: rows of the strict upper triangle.
+__host__ __device__ constexpr int packed_index(int i, int j) {
+    return i * (2 * kBeads - i - 1) / 2 + (j - i - 1);
+}
+
+// Row and column of packed element e (inverse of packed_index).
+__host__ __device__ inline void packed_row_col(int e, int &i, int &j) {
+    int r = 0;
+    while (r + 1 < kBeads - 1 && packed_index(r + 1, r + 2) <= e) ++r;
+    i = r;
+    j = e - packed_index(r, r + 1) + r + 1;
+}
+
+// Index of pair (p, q), p < q, among the O(O-1)/2 pairs of an O-bead block.
+__host__ __device__ constexpr int block_pair_index(int p, int q, int O) {
+    return p * (2 * O - p - 1) / 2 + (q - p - 1);
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11).  One round maps counter
+// (c0, c1, c2, c3) with key (k0, k1) to
+//   (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1, lo(M0 c0));
+// the key advances by the Weyl constants between rounds.
+constexpr uint32_t kPhiloxM0 = 0xD2511F53u;
+constexpr uint32_t kPhiloxM1 = 0xCD9E8D57u;
+constexpr uint32_t kPhiloxW0 = 0x9E3779B9u;
+constexpr uint32_t kPhiloxW1 = 0xBB67AE85u;
+
+struct Words4 {
+    uint32_t v0, v1, v2, v3;
+};
+
+__host__ __device__ __forceinline__ Words4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                                        uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t p0 = static_cast<uint64_t>(kPhiloxM0) * c0;
+        const uint64_t p1 = static_cast<uint64_t>(kPhiloxM1) * c2;
+        const uint32_t n0 = static_cast<uint32_t>(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n2 = static_cast<uint32_t>(p0 >> 32) ^ c3 ^ k1;
+        c1 = static_cast<uint32_t>(p1);
+        c3 = static_cast<uint32_t>(p0);
+        c0 = n0;
+        c2 = n2;
+        k0 += kPhiloxW0;
+        k1 += kPhiloxW1;
+    }
+    return Words4{c0, c1, c2, c3};
+}
+
+// Box-Muller (1958) on 24-bit uniforms u1 = ((ra >> 8) + 1) 2^-24 in (0, 1] and
+// u2 = (rb >> 8) 2^-24 in [0, 1), both exact in float32:
+//   zc = sqrt(-2 ln u1) cos(2 pi u2),  zs = sqrt(-2 ln u1) sin(2 pi u2).
+__device__ __forceinline__ void box_muller(uint32_t ra, uint32_t rb, float &zc, float &zs) {
+    const float u1 = static_cast<float>((ra >> 8) + 1u) * 0x1p-24f;
+    const float u2 = static_cast<float>(rb >> 8) * 0x1p-24f;
+    const float rad = sqrtf(-2.0f * logf(u1));
+    float s, c;
+    sincospif(2.0f * u2, &s, &c);
+    zc = rad * c;
+    zs = rad * s;
+}
+
+// Four standard normals of packed elements 4q .. 4q+3 of trajectory t.
+__device__ __forceinline__ float4 philox_normals(uint32_t q, uint32_t t, uint32_t slot, uint32_t k0, uint32_t k1) {
+    const Words4 r = philox4x32_10(q, t, slot, 0u, k0, k1);
+    float4 z;
+    box_muller(r.v0, r.v1, z.x, z.y);
+    box_muller(r.v2, r.v3, z.z, z.w);
+    return z;
+}
+
+// Workgroups are handed to the 8 XCDs round-robin (workgroup b runs on XCD
+// b % 8).  This bijection gives each XCD a contiguous range of logical
+// workgroup ids, so neighbouring logical work (the same region's references)
+// shares one XCD's L2.
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t n) {
+    constexpr uint32_t kXcd = 8;
+    const uint32_t per = n / kXcd, rem = n % kXcd;
+    const uint32_t x = b % kXcd, i = b / kXcd;
+    return x * per + (x < rem ? x : rem) + i;
+}
+
+// Coefficients of one guided DDIM step, rounded to float32 from float64 on
+// the host.  With a = abar_t, a' = abar_next:
+struct StepCoef {
+    float sa;       // sqrt(a)
+    float inv_s1a;  // 1 / sqrt(1 - a)
+    float s1a;      // sqrt(1 - a)
+    float inv_sa;   // 1 / sqrt(a)
+    float sap;      // sqrt(a')
+    float cdir;     // sqrt(max(0, 1 - a' - sigma^2))
+    float sigma;    // eta sqrt((1 - a') / (1 - a)) sqrt(1 - a / a')
+};
+
+struct StepArgs {
+    StepCoef c;
+    float w[kMaxGuidance];
+    int32_t R, G, S;
+    int32_t maps_per_block;   // independent layout: maps of one (r, g) per workgroup
+    int32_t blocks_per_rg;
+    uint32_t k0, k1, slot;    // Philox key words and step slot
+};
+
+struct ChainArgs {
+    int32_t chain_len;
+    int32_t overlap;
+    int32_t n_pairs;          // overlap (overlap - 1) / 2
+};
+
+// The fused stand-in denoiser + guidance + DDIM update of one element.
+__device__ __forceinline__ float ddim_cfg_element(float x, float x0c, float x0u, float w, const StepCoef &c, float z) {
+    const float eps_c = (x - c.sa * x0c) * c.inv_s1a;   // point-mass noise prediction, conditional
+    const float eps_u = (x - c.sa * x0u) * c.inv_s1a;   // ... unconditional
+    const float eps = eps_u + w * (eps_c - eps_u);      // classifier-free guidance
+    const float x0_hat = (x - c.s1a * eps) * c.inv_sa;  // predicted clean map
+    return c.sap * x0_hat + c.cdir * eps + c.sigma * z;
+}
+
+}  // namespace pc

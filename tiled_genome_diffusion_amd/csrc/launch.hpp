@@ -1,0 +1,26 @@
+// Host-side launchers of the kernels, one per translation unit; called by the
+// C ABI layer (api.hip) after it has validated every argument.
+#pragma once
+
+#include "common.hpp"
+
+namespace pc {
+
+hipError_t launch_fill(void *out, int64_t n_maps, uint32_t k0, uint32_t k1, uint32_t slot, bool raw,
+                       hipStream_t stream);
+
+hipError_t launch_step_indep(float *state, const float *x0c, const float *x0u, StepArgs a, bool noise,
+                             hipStream_t stream);
+
+hipError_t launch_step_chain(float *state, const float *x0c, const float *x0u, StepArgs a, ChainArgs ch,
+                             bool project, float *pre_disc, bool noise, hipStream_t stream);
+
+hipError_t launch_seam_project(float *state, int32_t n_chains, int32_t n_cols, ChainArgs ch, hipStream_t stream);
+
+hipError_t launch_seam_discrepancy(const float *state, int32_t n_chains, int32_t n_cols, ChainArgs ch, float *rms,
+                                   float *summary, hipStream_t stream);
+
+hipError_t launch_mds(const float *maps, int64_t n_maps, float *coords, float *eigvals, int32_t max_iters,
+                      hipStream_t stream);
+
+}  // namespace pc

@@ -1,0 +1,283 @@
+// Batched classical (Torgerson) MDS: one 64-lane workgroup per map, lane i
+// owning bead i.
+//
+//   1. The packed map is staged in LDS (504 coalesced float4 loads); lane i
+//      gathers row i of A = D o D into 64 VGPRs.
+//   2. Double centring B = J A J (times -1/2) from the row means (LDS) and the
+//      grand mean (wavefront reduction); row i of B stays in VGPRs.
+//   3. Block-4 subspace iteration with Rayleigh-Ritz: Z = B Q (Q broadcast
+//      from LDS, 256 FMAs per lane), H = Q^T Z by wavefront reductions, a 4x4
+//      Jacobi eigensolve (wave-uniform), Ritz vectors V = Q W, Y = Z W = B V,
+//      residuals ||Y_k - theta_k V_k||, and Q <- orth(Y) by modified
+//      Gram-Schmidt.  Stops when the residuals of the three largest Ritz pairs
+//      reach the float32 floor or after max_iters.
+//   4. The iteration finds the eigenvalues of largest magnitude.  If a
+//      negative one could hide a positive eigenvalue (the third largest Ritz
+//      value is below the smallest magnitude found), it reruns on B + mu I
+//      with mu >= -lambda_min, where magnitude order equals algebraic order.
+//   5. X = V_3 diag(sqrt(max(theta, 0))), each column signed so that its
+//      largest-magnitude entry is positive (lowest index on ties).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace pc {
+namespace {
+
+constexpr int kLanes = 64;
+constexpr int kBlk = 4;
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// Fixed pseudo-random start vectors (an integer hash of (bead, column)).
+__device__ __forceinline__ float start_vec(int i, int k) {
+    uint32_t x = static_cast<uint32_t>(i) * 0x9E3779B1u + static_cast<uint32_t>(k) * 0x85EBCA77u + 0x165667B1u;
+    x ^= x >> 16;
+    x *= 0x7FEB352Du;
+    x ^= x >> 15;
+    x *= 0x846CA68Bu;
+    x ^= x >> 16;
+    return static_cast<float>(x >> 8) * 0x1p-23f - 1.0f;
+}
+
+// Cyclic Jacobi on a symmetric 4x4 (values identical in every lane).
+// On return h is diagonal to float32 precision and w holds the eigenvectors
+// as columns.
+__device__ __forceinline__ void jacobi4(float (&h)[kBlk][kBlk], float (&w)[kBlk][kBlk]) {
+#pragma unroll
+    for (int r = 0; r < kBlk; ++r)
+#pragma unroll
+        for (int c = 0; c < kBlk; ++c) w[r][c] = r == c ? 1.f : 0.f;
+    for (int sweep = 0; sweep < 8; ++sweep) {
+        float off = 0.f, dia = 0.f;
+#pragma unroll
+        for (int r = 0; r < kBlk; ++r) {
+            dia += h[r][r] * h[r][r];
+#pragma unroll
+            for (int c = r + 1; c < kBlk; ++c) off += h[r][c] * h[r][c];
+        }
+        if (off <= 1e-14f * dia || off == 0.f) break;
+#pragma unroll
+        for (int p = 0; p < kBlk - 1; ++p) {
+#pragma unroll
+            for (int q = p + 1; q < kBlk; ++q) {
+                const float apq = h[p][q];
+                if (apq == 0.f) continue;
+                const float theta = (h[q][q] - h[p][p]) / (2.f * apq);
+                const float at = fabsf(theta);
+                const float t = at > 1e18f ? 0.5f / theta : copysignf(1.f, theta) / (at + sqrtf(theta * theta + 1.f));
+                const float c = 1.f / sqrtf(t * t + 1.f);
+                const float s = t * c;
+#pragma unroll
+                for (int r = 0; r < kBlk; ++r) {
+                    const float hp = h[r][p], hq = h[r][q];
+                    h[r][p] = c * hp - s * hq;
+                    h[r][q] = s * hp + c * hq;
+                }
+#pragma unroll
+                for (int r = 0; r < kBlk; ++r) {
+                    const float hp = h[p][r], hq = h[q][r];
+                    h[p][r] = c * hp - s * hq;
+                    h[q][r] = s * hp + c * hq;
+                }
+#pragma unroll
+                for (int r = 0; r < kBlk; ++r) {
+                    const float wp = w[r][p], wq = w[r][q];
+                    w[r][p] = c * wp - s * wq;
+                    w[r][q] = s * wp + c * wq;
+                }
+            }
+        }
+    }
+}
+
+// Modified Gram-Schmidt of the four per-lane columns y into q.  A column that
+// vanishes is replaced by its start vector.
+__device__ __forceinline__ void orthonormalise(int lane, const float (&y)[kBlk], float (&q)[kBlk]) {
+#pragma unroll
+    for (int k = 0; k < kBlk; ++k) {
+        float v = y[k];
+        for (int attempt = 0; attempt < 2; ++attempt) {
+#pragma unroll
+            for (int l = 0; l < k; ++l) v -= wave_sum(q[l] * v) * q[l];
+            const float n2 = wave_sum(v * v);
+            if (n2 > 1e-30f) {
+                v *= 1.f / sqrtf(n2);
+                break;
+            }
+            v = start_vec(lane, k);
+            if (attempt == 1) v = 0.f;
+        }
+        q[k] = v;
+    }
+}
+
+// Block-4 subspace iteration with Rayleigh-Ritz on B + mu I.  On return
+// theta (descending, shift included) and vec (lane = bead) hold the Ritz
+// pairs; the result is the smallest Ritz magnitude found.
+__device__ __forceinline__ float subspace(const float (&b)[kBeads], float mu, int32_t max_iters, int lane,
+                                          float4 *s_q, float (&theta)[kBlk], float (&vec)[kBlk]) {
+    float q[kBlk];
+    {
+        float y0[kBlk];
+#pragma unroll
+        for (int k = 0; k < kBlk; ++k) y0[k] = start_vec(lane, k);
+        orthonormalise(lane, y0, q);
+    }
+    float rho = 0.f;
+    for (int it = 0; it < max_iters; ++it) {
+        s_q[lane] = make_float4(q[0], q[1], q[2], q[3]);
+        __syncthreads();
+        float z[kBlk] = {mu * q[0], mu * q[1], mu * q[2], mu * q[3]};
+#pragma unroll
+        for (int j = 0; j < kBeads; ++j) {
+            const float4 qj = s_q[j];
+            z[0] = fmaf(b[j], qj.x, z[0]);
+            z[1] = fmaf(b[j], qj.y, z[1]);
+            z[2] = fmaf(b[j], qj.z, z[2]);
+            z[3] = fmaf(b[j], qj.w, z[3]);
+        }
+        __syncthreads();
+        // H = Q^T (B + mu I) Q, symmetrised.
+        float h[kBlk][kBlk], w[kBlk][kBlk];
+#pragma unroll
+        for (int r = 0; r < kBlk; ++r)
+#pragma unroll
+            for (int c = r; c < kBlk; ++c) {
+                const float s = wave_sum(q[r] * z[c] + q[c] * z[r]) * 0.5f;
+                h[r][c] = s;
+                h[c][r] = s;
+            }
+        jacobi4(h, w);
+        float d[kBlk] = {h[0][0], h[1][1], h[2][2], h[3][3]};
+        // Sort descending, carrying the eigenvector columns (selects only).
+#pragma unroll
+        for (int x = 0; x < kBlk - 1; ++x)
+#pragma unroll
+            for (int y = 0; y < kBlk - 1 - x; ++y) {
+                const bool sw = d[y + 1] > d[y];
+                const float t = d[y];
+                d[y] = sw ? d[y + 1] : d[y];
+                d[y + 1] = sw ? t : d[y + 1];
+#pragma unroll
+                for (int r = 0; r < kBlk; ++r) {
+                    const float u = w[r][y];
+                    w[r][y] = sw ? w[r][y + 1] : u;
+                    w[r][y + 1] = sw ? u : w[r][y + 1];
+                }
+            }
+        float yv[kBlk];
+        float thmax = 0.f;
+        rho = 3.4e38f;
+#pragma unroll
+        for (int k = 0; k < kBlk; ++k) {
+            vec[k] = q[0] * w[0][k] + q[1] * w[1][k] + q[2] * w[2][k] + q[3] * w[3][k];
+            yv[k] = z[0] * w[0][k] + z[1] * w[1][k] + z[2] * w[2][k] + z[3] * w[3][k];
+            theta[k] = d[k];
+            thmax = fmaxf(thmax, fabsf(d[k]));
+            rho = fminf(rho, fabsf(d[k]));
+        }
+        const float tol = 4e-6f * thmax;
+        bool done = it >= 1;
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            const float r = yv[k] - d[k] * vec[k];
+            done = done && wave_sum(r * r) <= tol * tol;
+        }
+        if (done) break;
+        orthonormalise(lane, yv, q);
+    }
+    return rho;
+}
+
+__global__ __launch_bounds__(kLanes) void k_mds(const float *__restrict__ maps, float *__restrict__ coords,
+                                                float *__restrict__ eigvals, int32_t max_iters) {
+    __shared__ float4 s_map[kQuads];
+    __shared__ float4 s_q[kBeads];
+    __shared__ float s_mean[kBeads];
+    const int i = threadIdx.x;
+    const size_t m = blockIdx.x;
+
+    const float4 *src = reinterpret_cast<const float4 *>(maps + m * kPacked);
+    for (int k = i; k < kQuads; k += kLanes) s_map[k] = src[k];
+    __syncthreads();
+    const float *xs = reinterpret_cast<const float *>(s_map);
+
+    // Row i of A = D o D.
+    float b[kBeads];
+    const int base_i = packed_index(i, i + 1) - i - 1;  // idx(i, j) = base_i + j for j > i
+    float rsum = 0.f;
+#pragma unroll
+    for (int j = 0; j < kBeads; ++j) {
+        const int cj = packed_index(j, j + 1) - j - 1;  // idx(j, i) = cj + i for j < i
+        int addr = j < i ? cj + i : base_i + j;
+        addr = j == i ? 0 : addr;
+        const float d = xs[addr];
+        b[j] = j == i ? 0.f : d * d;
+        rsum += b[j];
+    }
+    s_mean[i] = rsum * (1.f / kBeads);
+    const float gmean = wave_sum(rsum) * (1.f / (kBeads * kBeads));
+    __syncthreads();
+    const float mean_i = s_mean[i];
+#pragma unroll
+    for (int j = 0; j < kBeads; ++j) b[j] = -0.5f * (b[j] - mean_i - s_mean[j] + gmean);
+
+    float theta[kBlk], vec[kBlk];
+    const float rho = subspace(b, 0.f, max_iters, i, s_q, theta, vec);
+    // The iteration finds the eigenvalues of largest magnitude; any eigenvalue
+    // it missed has magnitude <= rho.  If the third largest Ritz value is below
+    // rho, a missed positive eigenvalue could outrank it: iterate on B + mu I,
+    // mu >= -lambda_min, where magnitude order is algebraic order.  Below
+    // 1e-6 of the largest Ritz value the spectrum is float32 noise and no
+    // rerun is needed.
+    if (theta[2] < rho && rho > 1e-6f * fabsf(theta[0])) {
+        const float mu = fmaxf(-theta[3], rho);
+        subspace(b, mu, max_iters, i, s_q, theta, vec);
+#pragma unroll
+        for (int k = 0; k < kBlk; ++k) theta[k] -= mu;
+    }
+
+    // Sign each column by its largest-magnitude entry (lowest bead on ties).
+    float out[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        float best = fabsf(vec[k]);
+        int arg = i;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const float ob = __shfl_xor(best, o);
+            const int oa = __shfl_xor(arg, o);
+            if (ob > best || (ob == best && oa < arg)) {
+                best = ob;
+                arg = oa;
+            }
+        }
+        const float sv = __shfl(vec[k], arg);
+        out[k] = (sv < 0.f ? -vec[k] : vec[k]) * sqrtf(fmaxf(theta[k], 0.f));
+    }
+    float *dst = coords + (m * kBeads + i) * 3;
+    dst[0] = out[0];
+    dst[1] = out[1];
+    dst[2] = out[2];
+    if (eigvals && i == 0) {
+        eigvals[m * 3 + 0] = theta[0];
+        eigvals[m * 3 + 1] = theta[1];
+        eigvals[m * 3 + 2] = theta[2];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_mds(const float *maps, int64_t n_maps, float *coords, float *eigvals, int32_t max_iters,
+                      hipStream_t stream) {
+    if (n_maps == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_mds, dim3(static_cast<uint32_t>(n_maps)), dim3(kLanes), 0, stream, maps, coords, eigvals,
+                       max_iters);
+    return hipGetLastError();
+}
+
+}  // namespace pc

@@ -1,0 +1,117 @@
+// Standalone seam kernels: overlap-consistency projection and the per-seam
+// RMS discrepancy with a fixed-order summary reduction.  The fused variants
+// live in the chain step kernel; these serve projections every K > 1 steps,
+// post-projection checks and states produced elsewhere.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace pc {
+namespace {
+
+__device__ __forceinline__ void pair_indices(int p, int O, int &lidx, int &ridx) {
+    int pp = 0;
+    while (pp + 2 < O && block_pair_index(pp + 1, pp + 2, O) <= p) ++pp;
+    const int qq = p - block_pair_index(pp, pp + 1, O) + pp + 1;
+    lidx = packed_index(kBeads - O + pp, kBeads - O + qq);
+    ridx = packed_index(pp, qq);
+}
+
+// One lane per (chain, seam, column, pair).
+__global__ __launch_bounds__(256) void k_seam_project(float *__restrict__ state, int64_t total, int32_t n_cols,
+                                                      ChainArgs ch) {
+    const int64_t it = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (it >= total) return;
+    const int NP = ch.n_pairs, L = ch.chain_len;
+    const int p = static_cast<int>(it % NP);
+    const int64_t sc = it / NP;                 // ((c (L-1) + j) n_cols + col)
+    const int col = static_cast<int>(sc % n_cols);
+    const int64_t cj = sc / n_cols;
+    const int64_t c = cj / (L - 1);
+    const int64_t j = cj - c * (L - 1);
+    int li, ri;
+    pair_indices(p, ch.overlap, li, ri);
+    const size_t map_l = static_cast<size_t>((c * L + j) * n_cols + col);
+    const size_t map_r = map_l + n_cols;
+    const float m = (state[map_l * kPacked + li] + state[map_r * kPacked + ri]) * 0.5f;
+    state[map_l * kPacked + li] = m;
+    state[map_r * kPacked + ri] = m;
+}
+
+// One lane per (chain, seam, column): RMS over the seam's pairs, in pair order.
+__global__ __launch_bounds__(256) void k_seam_disc(const float *__restrict__ state, int64_t total, int32_t n_cols,
+                                                   ChainArgs ch, float *__restrict__ rms) {
+    const int64_t sc = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (sc >= total) return;
+    const int L = ch.chain_len, NP = ch.n_pairs, O = ch.overlap;
+    const int col = static_cast<int>(sc % n_cols);
+    const int64_t cj = sc / n_cols;
+    const int64_t c = cj / (L - 1);
+    const int64_t j = cj - c * (L - 1);
+    const float *xl = state + static_cast<size_t>((c * L + j) * n_cols + col) * kPacked;
+    const float *xr = xl + static_cast<size_t>(n_cols) * kPacked;
+    float acc = 0.f;
+    int p = 0;
+    for (int pp = 0; pp < O; ++pp)
+        for (int qq = pp + 1; qq < O; ++qq, ++p) {
+            const float d = xl[packed_index(kBeads - O + pp, kBeads - O + qq)] - xr[packed_index(pp, qq)];
+            acc = fmaf(d, d, acc);
+        }
+    rms[sc] = sqrtf(acc / static_cast<float>(NP));
+}
+
+// Mean and max of n values by one workgroup: each lane folds a strided slice
+// in index order, then a fixed tree over the lanes.  Deterministic.
+__global__ __launch_bounds__(256) void k_mean_max(const float *__restrict__ v, int64_t n, float *__restrict__ out) {
+    __shared__ double s_sum[256];
+    __shared__ float s_max[256];
+    double acc = 0.0;
+    float mx = 0.f;
+    for (int64_t i = threadIdx.x; i < n; i += 256) {
+        acc += v[i];
+        mx = fmaxf(mx, v[i]);
+    }
+    s_sum[threadIdx.x] = acc;
+    s_max[threadIdx.x] = mx;
+    __syncthreads();
+    for (int h = 128; h > 0; h >>= 1) {
+        if (static_cast<int>(threadIdx.x) < h) {
+            s_sum[threadIdx.x] += s_sum[threadIdx.x + h];
+            s_max[threadIdx.x] = fmaxf(s_max[threadIdx.x], s_max[threadIdx.x + h]);
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        out[0] = n > 0 ? static_cast<float>(s_sum[0] / static_cast<double>(n)) : 0.f;
+        out[1] = s_max[0];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_seam_project(float *state, int32_t n_chains, int32_t n_cols, ChainArgs ch, hipStream_t stream) {
+    const int64_t total = static_cast<int64_t>(n_chains) * (ch.chain_len - 1) * n_cols * ch.n_pairs;
+    if (total == 0) return hipSuccess;
+    const int64_t blocks = (total + 255) / 256;
+    hipLaunchKernelGGL(k_seam_project, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream, state, total,
+                       n_cols, ch);
+    return hipGetLastError();
+}
+
+hipError_t launch_seam_discrepancy(const float *state, int32_t n_chains, int32_t n_cols, ChainArgs ch, float *rms,
+                                   float *summary, hipStream_t stream) {
+    const int64_t total = static_cast<int64_t>(n_chains) * (ch.chain_len - 1) * n_cols;
+    if (total > 0) {
+        const int64_t blocks = (total + 255) / 256;
+        hipLaunchKernelGGL(k_seam_disc, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream, state, total,
+                           n_cols, ch, rms);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (summary) {
+        hipLaunchKernelGGL(k_mean_max, dim3(1), dim3(256), 0, stream, rms, total, summary);
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
+}  // namespace pc
