@@ -50,9 +50,9 @@ def normwise_err(gpu: np.ndarray, ref: np.ndarray) -> float:
 
 
 def run_steps(wl: Workload, seed: int, n_steps: int, sample_idx, record, project: bool = True, pre_disc=False,
-              refs=None):
-    """Run the HIP sampler step by step; return ({step: state rows at sample_idx}, final state tensor,
-    {step: pre-projection RMS tensor (cpu)})."""
+              refs=None, stop_after: int | None = None):
+    """Run the HIP sampler step by step (the first ``stop_after`` steps of an n_steps schedule, all by
+    default); return ({step: state rows at sample_idx}, final state tensor, {step: pre-projection RMS})."""
     torch, dev = torch_dev()
     lay = layout_of(wl)
     if refs is None:
@@ -70,7 +70,7 @@ def run_steps(wl: Workload, seed: int, n_steps: int, sample_idx, record, project
     chains = wl.chain_len > 1
     disc_buf = torch.empty(lay.n_seams * lay.n_guidance * lay.n_traj, dtype=torch.float32, device=dev) \
         if (chains and pre_disc) else None
-    for i in range(n_steps):
+    for i in range(n_steps if stop_after is None else stop_after):
         pc.pc_ddim_cfg_step(state, x0c_d, x0u_d, list(wl.w), lay, a_t[i], a_n[i], wl.eta, seed, i + 1,
                             project_seams=chains and project, pre_disc=disc_buf)
         if i + 1 in record:

@@ -67,7 +67,7 @@ def test_projection_invariants_full_size():
     say("projection invariants on 16,384 maps")
     refs = upload_refs(wl, 1)
     # same keys, with and without projection on the final step
-    _, base, _ = run_steps(wl, 1, 49, [0], set(), refs=refs)
+    _, base, _ = run_steps(wl, 1, 50, [0], set(), refs=refs, stop_after=49)
     a_t, a_n = pc.pc_ddim_schedule(50)
     noproj = base.clone()
     pc.pc_ddim_cfg_step(noproj, refs[2], refs[3], list(wl.w), lay, a_t[49], a_n[49], 1.0, 1, 50,

@@ -1,7 +1,9 @@
 """Compile the HIP library libpc.so for gfx950, in-tree.
 
 One shared library holds every kernel and the C ABI of include/pc.h.  All
-HIP code is built with packed-FP32 instructions disabled.
+HIP code is built with packed-FP32 instructions disabled and without implicit
+FMA contraction (kernels spell out their fused multiply-adds, so every kernel
+that computes a value rounds it the same way).
 """
 
 from __future__ import annotations
@@ -28,6 +30,7 @@ def hipcc() -> str:
 
 def command(out: str = LIB) -> list[str]:
     return [hipcc(), "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared", "-fvisibility=hidden",
+            "-ffp-contract=off",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-Wall", "-Wno-unknown-pragmas",
             "-I", os.path.join(ROOT, "include"),
