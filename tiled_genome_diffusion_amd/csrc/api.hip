@@ -7,7 +7,7 @@
 
 #include <new>
 
-#include "../../include/pc.h"
+#include "pc.h"
 #include "common.hpp"
 #include "launch.hpp"
 

@@ -13,12 +13,35 @@ namespace pc {
 namespace {
 
 constexpr int kThreads = 512;
+constexpr int kIndepU = 2;           // maps in flight per lane, independent layout
+constexpr int kIndepMaps = 2;        // maps of one (region, weight) per workgroup
+constexpr int kChainCh = 8;          // tiles per barrier interval, chain layout
+// States well beyond the 256 MB Infinity Cache are streamed with
+// non-temporal loads and stores: each value is touched once per step, so
+// caching it only evicts the references.  Smaller states stay cacheable, so
+// consecutive steps can hit in the Infinity Cache (measured: a 258 MB chain
+// state steps 8% faster cached than streamed).
+constexpr size_t kStreamBytes = size_t(512) << 20;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float4 ld4(const float *p, size_t quad) {
     return reinterpret_cast<const float4 *>(p)[quad];
 }
 __device__ __forceinline__ void st4(float *p, size_t quad, float4 v) {
     reinterpret_cast<float4 *>(p)[quad] = v;
+}
+template <bool NT>
+__device__ __forceinline__ float4 ld_state(const float *p, size_t quad) {
+    if (!NT) return ld4(p, quad);
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p) + quad);
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+template <bool NT>
+__device__ __forceinline__ void st_state(float *p, size_t quad, float4 v) {
+    if (!NT) return st4(p, quad, v);
+    const f32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<f32x4 *>(p) + quad);
 }
 
 __device__ __forceinline__ float4 step4(float4 x, float4 xc, float4 xu, float w, const StepCoef &c, float4 z) {
@@ -33,7 +56,7 @@ __device__ __forceinline__ float4 step4(float4 x, float4 xc, float4 xu, float w,
 // ---------------------------------------------------------------------------
 // Fills: raw Philox words or normals of one slot for maps [m0, m1) of a
 // workgroup.  MODE 0 writes normals (float4), MODE 1 raw words (uint4).
-template <int MODE>
+template <int MODE, bool NT>
 __global__ __launch_bounds__(kThreads) void k_fill(void *__restrict__ out, int64_t n_maps, int32_t maps_per_block,
                                                    uint32_t k0, uint32_t k1, uint32_t slot) {
     const uint32_t q = threadIdx.x;
@@ -44,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void k_fill(void *__restrict__ out, int64
     for (int64_t m = m0; m < m1; ++m) {
         const size_t quad = static_cast<size_t>(m) * kQuads + q;
         if (MODE == 0) {
-            st4(static_cast<float *>(out), quad, philox_normals(q, static_cast<uint32_t>(m), slot, k0, k1));
+            st_state<NT>(static_cast<float *>(out), quad, philox_normals(q, static_cast<uint32_t>(m), slot, k0, k1));
         } else {
             const Words4 r = philox4x32_10(q, static_cast<uint32_t>(m), slot, 0u, k0, k1);
             reinterpret_cast<uint4 *>(out)[quad] = make_uint4(r.v0, r.v1, r.v2, r.v3);
@@ -55,20 +78,20 @@ __global__ __launch_bounds__(kThreads) void k_fill(void *__restrict__ out, int64
 // ---------------------------------------------------------------------------
 // Independent maps: workgroup -> (region r, weight g, chunk of trajectories).
 // U maps are loaded before any is computed, to keep U loads in flight.
-template <int U, bool NOISE>
+template <int U, bool NOISE, bool NT>
 __device__ __forceinline__ void step_maps(float *__restrict__ state, size_t map0, uint32_t t0, uint32_t q, float4 xc,
                                           float4 xu, float w, const StepArgs &a) {
     float4 x[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) x[u] = ld4(state, (map0 + u) * kQuads + q);
+    for (int u = 0; u < U; ++u) x[u] = ld_state<NT>(state, (map0 + u) * kQuads + q);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const float4 z = NOISE ? philox_normals(q, t0 + u, a.slot, a.k0, a.k1) : make_float4(0.f, 0.f, 0.f, 0.f);
-        st4(state, (map0 + u) * kQuads + q, step4(x[u], xc, xu, w, a.c, z));
+        st_state<NT>(state, (map0 + u) * kQuads + q, step4(x[u], xc, xu, w, a.c, z));
     }
 }
 
-template <int U, bool NOISE>
+template <int U, bool NOISE, bool NT>
 __global__ __launch_bounds__(kThreads) void k_step_indep(float *__restrict__ state, const float *__restrict__ x0c,
                                                          const float *__restrict__ x0u, StepArgs a) {
     const uint32_t q = threadIdx.x;
@@ -85,8 +108,8 @@ __global__ __launch_bounds__(kThreads) void k_step_indep(float *__restrict__ sta
     const int s1 = s0 + a.maps_per_block < a.S ? s0 + a.maps_per_block : a.S;
     const uint32_t t_base = static_cast<uint32_t>(rg) * static_cast<uint32_t>(a.S);
     int s = s0;
-    for (; s + U <= s1; s += U) step_maps<U, NOISE>(state, t_base + s, t_base + s, q, xc, xu, w, a);
-    for (; s < s1; ++s) step_maps<1, NOISE>(state, t_base + s, t_base + s, q, xc, xu, w, a);
+    for (; s + U <= s1; s += U) step_maps<U, NOISE, NT>(state, t_base + s, t_base + s, q, xc, xu, w, a);
+    for (; s < s1; ++s) step_maps<1, NOISE, NT>(state, t_base + s, t_base + s, q, xc, xu, w, a);
 }
 
 // ---------------------------------------------------------------------------
@@ -97,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void k_step_indep(float *__restrict__ sta
 // tiles, otherwise each copy is written back unchanged.  With DISC the RMS of
 // (left - right) over the seam's pairs is stored per (seam, g, s), summed in
 // pair order by one lane.
-template <int CH, bool PROJECT, bool DISC, bool NOISE>
+template <int CH, bool PROJECT, bool DISC, bool NOISE, bool NT>
 __global__ __launch_bounds__(kThreads) void k_step_chain(float *__restrict__ state, const float *__restrict__ x0c,
                                                          const float *__restrict__ x0u, StepArgs a, ChainArgs ch,
                                                          float *__restrict__ pre_disc) {
@@ -147,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void k_step_chain(float *__restrict__ sta
             float4 x[CH];
 #pragma unroll
             for (int u = 0; u < CH; ++u)
-                if (u < nk) x[u] = ld4(state, (col_map0 + static_cast<size_t>(k0 + u) * n_cols) * kQuads + q);
+                if (u < nk) x[u] = ld_state<NT>(state, (col_map0 + static_cast<size_t>(k0 + u) * n_cols) * kQuads + q);
 #pragma unroll
             for (int u = 0; u < CH; ++u) {
                 if (u >= nk) break;
@@ -162,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void k_step_chain(float *__restrict__ sta
                 const bool lft = has_left && k > 0;
                 const bool rgt = has_right && k < L - 1;
                 if (!lft && !rgt) {
-                    st4(state, map * kQuads + q, y);
+                    st_state<NT>(state, map * kQuads + q, y);
                 } else {
                     const float v[4] = {y.x, y.y, y.z, y.w};
                     const int slot = k % (CH + 1);
@@ -225,47 +248,58 @@ hipError_t launch_fill(void *out, int64_t n_maps, uint32_t k0, uint32_t k1, uint
                        hipStream_t stream) {
     constexpr int kMpb = 4;
     const int64_t blocks = (n_maps + kMpb - 1) / kMpb;
+    const dim3 grid(static_cast<uint32_t>(blocks));
+    const bool nt = static_cast<size_t>(n_maps) * kPacked * 4 > kStreamBytes;
     if (raw)
-        hipLaunchKernelGGL(k_fill<1>, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream, out, n_maps,
-                           kMpb, k0, k1, slot);
+        hipLaunchKernelGGL((k_fill<1, false>), grid, dim3(kThreads), 0, stream, out, n_maps, kMpb, k0, k1, slot);
+    else if (nt)
+        hipLaunchKernelGGL((k_fill<0, true>), grid, dim3(kThreads), 0, stream, out, n_maps, kMpb, k0, k1, slot);
     else
-        hipLaunchKernelGGL(k_fill<0>, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream, out, n_maps,
-                           kMpb, k0, k1, slot);
+        hipLaunchKernelGGL((k_fill<0, false>), grid, dim3(kThreads), 0, stream, out, n_maps, kMpb, k0, k1, slot);
     return hipGetLastError();
 }
 
 hipError_t launch_step_indep(float *state, const float *x0c, const float *x0u, StepArgs a, bool noise,
                              hipStream_t stream) {
-    constexpr int kU = 2;
-    a.maps_per_block = 8;
+    a.maps_per_block = kIndepMaps;
     a.blocks_per_rg = (a.S + a.maps_per_block - 1) / a.maps_per_block;
+    const int64_t n_maps = static_cast<int64_t>(a.R) * a.G * a.S;
     const int64_t blocks = static_cast<int64_t>(a.R) * a.G * a.blocks_per_rg;
     const dim3 grid(static_cast<uint32_t>(blocks));
-    if (noise)
-        hipLaunchKernelGGL((k_step_indep<kU, true>), grid, dim3(kThreads), 0, stream, state, x0c, x0u, a);
-    else
-        hipLaunchKernelGGL((k_step_indep<kU, false>), grid, dim3(kThreads), 0, stream, state, x0c, x0u, a);
+    const bool nt = static_cast<size_t>(n_maps) * kPacked * 4 > kStreamBytes;
+#define PC_INDEP(N, T) \
+    hipLaunchKernelGGL((k_step_indep<kIndepU, N, T>), grid, dim3(kThreads), 0, stream, state, x0c, x0u, a)
+    if (noise) {
+        if (nt) PC_INDEP(true, true); else PC_INDEP(true, false);
+    } else {
+        if (nt) PC_INDEP(false, true); else PC_INDEP(false, false);
+    }
+#undef PC_INDEP
     return hipGetLastError();
 }
 
 hipError_t launch_step_chain(float *state, const float *x0c, const float *x0u, StepArgs a, ChainArgs ch,
                              bool project, float *pre_disc, bool noise, hipStream_t stream) {
-    constexpr int kCh = 4;
+    const int64_t n_maps = static_cast<int64_t>(a.R) * a.G * a.S;
     const int64_t blocks = static_cast<int64_t>(a.R / ch.chain_len) * a.G * a.S;
     const dim3 grid(static_cast<uint32_t>(blocks));
     const bool disc = pre_disc != nullptr;
-#define PC_CHAIN(P, D, N)                                                                                   \
-    hipLaunchKernelGGL((k_step_chain<kCh, P, D, N>), grid, dim3(kThreads), 0, stream, state, x0c, x0u, a, ch, \
-                       pre_disc)
+    const bool nt = static_cast<size_t>(n_maps) * kPacked * 4 > kStreamBytes;
+#define PC_CHAIN(P, D, N, T)                                                                                    \
+    hipLaunchKernelGGL((k_step_chain<kChainCh, P, D, N, T>), grid, dim3(kThreads), 0, stream, state, x0c, x0u, a, \
+                       ch, pre_disc)
+#define PC_CHAIN_NT(P, D, N) \
+    if (nt) PC_CHAIN(P, D, N, true); else PC_CHAIN(P, D, N, false)
     if (project) {
         if (disc) {
-            if (noise) PC_CHAIN(true, true, true); else PC_CHAIN(true, true, false);
+            if (noise) PC_CHAIN_NT(true, true, true); else PC_CHAIN_NT(true, true, false);
         } else {
-            if (noise) PC_CHAIN(true, false, true); else PC_CHAIN(true, false, false);
+            if (noise) PC_CHAIN_NT(true, false, true); else PC_CHAIN_NT(true, false, false);
         }
     } else {
-        if (noise) PC_CHAIN(false, true, true); else PC_CHAIN(false, true, false);
+        if (noise) PC_CHAIN_NT(false, true, true); else PC_CHAIN_NT(false, true, false);
     }
+#undef PC_CHAIN_NT
 #undef PC_CHAIN
     return hipGetLastError();
 }
