@@ -15,6 +15,8 @@ bounded sample of the same workload on the host.
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -39,7 +41,47 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target duration of the oracle baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-only", action="store_true",
+                   help="time a plain device-to-device copy of the workload's state size instead "
+                        "(the calibration kernel for the HBM byte counters)")
     return p.parse_args()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per step launch from the committed FETCH_SIZE/WRITE_SIZE counter runs
+    (profiles/*_traffic.json), or None if none matches this workload or the kernel
+    source has changed since the counters were taken."""
+    for path in glob.glob(os.path.join(ROOT, "profiles", "*_traffic.json")):
+        with open(path) as f:
+            d = json.load(f)
+        if d.get("workload") != workload:
+            continue
+        h = hashlib.sha256()
+        for rel in d["source_files"]:
+            with open(os.path.join(ROOT, rel), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() == d["source_sha256"]:
+            return d["traffic_bytes_per_launch"], d["kernel"]
+    return None, None
+
+
+def copy_only(args, wl):
+    """A plain copy of known size: the reference for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+
+    n = wl.n_maps * 2016
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "ms": dt * 1e3,
+                      "gbs": 2 * n * 4 / dt / 1e9, "workload": wl.name}), flush=True)
 
 
 def cpu_baseline(wl, n_steps, seed, target_s):
@@ -106,6 +148,8 @@ def main():
     from workloads import get, reference_maps
 
     wl = get(args.workload)
+    if args.copy_only:
+        return copy_only(args, wl)
     n_steps = args.n_steps or wl.n_steps[0]
     dev = torch.device("cuda:0")
     lay = pc.PCLayout(wl.n_regions, wl.n_guidance, wl.n_traj, wl.chain_len, wl.overlap if wl.chain_len > 1 else 0)
@@ -147,6 +191,7 @@ def main():
     bytes_per_launch = lay.n_maps * STEP_BYTES_PER_MAP + lay.n_regions * REF_BYTES_PER_REGION
     achieved = bytes_per_launch / (launch_ms * 1e-3) / 1e9
     traj_steps = lay.n_maps * n_steps
+    traffic, traffic_kernel = measured_traffic(wl.name)
 
     out = {
         "metric": "DDIM trajectory-steps/s (64-bead maps) + % HBM peak; MDS maps/s",
@@ -161,7 +206,9 @@ def main():
                    "seed": args.seed, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "k_step_indep" if wl.chain_len == 1 else "k_step_chain",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None, "launch_us": launch_ms * 1e3, "bytes_per_launch": bytes_per_launch},
+                     "traffic": traffic, "traffic_unit": "bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-scaled)",
+                     "traffic_kernel": traffic_kernel, "launch_us": launch_ms * 1e3,
+                     "bytes_per_launch": bytes_per_launch},
         "step_loop_traj_steps_per_s": traj_steps / (step_ms * 1e-3),
         "mds_maps_per_s": lay.n_maps / (mds_ms * 1e-3),
         "mds_ms": mds_ms,
