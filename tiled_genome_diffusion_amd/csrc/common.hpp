@@ -19,12 +19,28 @@ __host__ __device__ constexpr int packed_index(int i, int j) {
     return i * (2 * kBeads - i - 1) / 2 + (j - i - 1);
 }
 
-// Row and column of packed element e (inverse of packed_index).
+// Row and column of packed element e (inverse of packed_index).  Row i starts
+// at i (2n - i - 1) / 2, so i is the floor of the smaller root of that
+// quadratic; a float estimate is corrected by at most one step each way.
 __host__ __device__ inline void packed_row_col(int e, int &i, int &j) {
-    int r = 0;
-    while (r + 1 < kBeads - 1 && packed_index(r + 1, r + 2) <= e) ++r;
+    constexpr int b = 2 * kBeads - 1;
+    int r = static_cast<int>((b - sqrtf(static_cast<float>(b * b - 8 * e))) * 0.5f);
+    r = r < 0 ? 0 : (r > kBeads - 2 ? kBeads - 2 : r);
+    if (r < kBeads - 2 && packed_index(r + 1, r + 2) <= e) ++r;
+    if (r > 0 && packed_index(r, r + 1) > e) --r;
     i = r;
     j = e - packed_index(r, r + 1) + r + 1;
+}
+
+// Inverse of block_pair_index: pair p of an O-bead block -> (pp, qq).
+__host__ __device__ inline void block_pair_row_col(int p, int O, int &pp, int &qq) {
+    const int b = 2 * O - 1;
+    int r = static_cast<int>((b - sqrtf(static_cast<float>(b * b - 8 * p))) * 0.5f);
+    r = r < 0 ? 0 : (r > O - 2 ? O - 2 : r);
+    if (r < O - 2 && (r + 1) * (2 * O - r - 2) / 2 <= p) ++r;
+    if (r > 0 && r * (2 * O - r - 1) / 2 > p) --r;
+    pp = r;
+    qq = p - r * (2 * O - r - 1) / 2 + r + 1;
 }
 
 // Index of pair (p, q), p < q, among the O(O-1)/2 pairs of an O-bead block.

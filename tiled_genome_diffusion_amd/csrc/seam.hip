@@ -9,9 +9,8 @@ namespace pc {
 namespace {
 
 __device__ __forceinline__ void pair_indices(int p, int O, int &lidx, int &ridx) {
-    int pp = 0;
-    while (pp + 2 < O && block_pair_index(pp + 1, pp + 2, O) <= p) ++pp;
-    const int qq = p - block_pair_index(pp, pp + 1, O) + pp + 1;
+    int pp, qq;
+    block_pair_row_col(p, O, pp, qq);
     lidx = packed_index(kBeads - O + pp, kBeads - O + qq);
     ridx = packed_index(pp, qq);
 }

@@ -15,7 +15,12 @@ namespace {
 constexpr int kThreads = 512;
 constexpr int kIndepU = 2;           // maps in flight per lane, independent layout
 constexpr int kIndepMaps = 2;        // maps of one (region, weight) per workgroup
-constexpr int kChainCh = 8;          // tiles per barrier interval, chain layout
+constexpr int kChainU = 2;           // maps in flight per lane, chain layout
+// Maps of one (tile, weight) per workgroup, chain layout: enough to amortise
+// the per-workgroup set-up and barriers, while keeping about kChainGrid
+// workgroups in the grid (measured best on MI355X: 8 for 16,384 maps, 16 for
+// 32,000).
+constexpr int kChainMapsMin = 4, kChainMapsMax = 16, kChainGrid = 2048;
 // States well beyond the 256 MB Infinity Cache are streamed with
 // non-temporal loads and stores: each value is touched once per step, so
 // caching it only evicts the references.  Smaller states stay cacheable, so
@@ -113,42 +118,52 @@ __global__ __launch_bounds__(kThreads) void k_step_indep(float *__restrict__ sta
 }
 
 // ---------------------------------------------------------------------------
-// Chains: one workgroup per joint sample (chain c, weight g, trajectory s),
-// walking the chain's tiles CH at a time.  Stepped values of seam entries go
-// to LDS instead of memory; after a barrier, seam j (tiles j, j+1) is
-// resolved from both copies: with PROJECT the float32 mean is written to both
-// tiles, otherwise each copy is written back unchanged.  With DISC the RMS of
-// (left - right) over the seam's pairs is stored per (seam, g, s), summed in
-// pair order by one lane.
-template <int CH, bool PROJECT, bool DISC, bool NOISE, bool NT>
+// Chains.  Workgroups are laid out as for independent maps: one workgroup
+// steps a.maps_per_block maps of one tile k (region r = c L + k) and weight g.
+// Ownership is by 128-byte line (8 quads; a map is 63 lines): a line is a
+// "seam line" if it holds any element of the left seam (pairs of beads
+// 0..O-1).  Seam k, shared by tiles k and k+1, is resolved entirely by tile
+// k's workgroup:
+//   * lanes of plain and right-seam lines step tile k's quads; right-seam
+//     values (beads 64-O..63) go to LDS;
+//   * lanes of seam lines step tile k+1's quads instead (with tile k+1's
+//     noise and references) and put its left-seam values in LDS; tile k+1's
+//     workgroup skips those lines, and tile 0 steps them for itself too;
+//   * after one barrier both sides form the float32 mean (left + right) * 0.5
+//     (with PROJECT; otherwise each copy keeps its stepped value) and store
+//     whole float4 quads.
+// Every quad is stepped once, every store is a full float4, and no cache line
+// is written by two workgroups.  Each lane runs one stepping task per map
+// (two only in tile 0's seam lines), so waves stay in lockstep.  With DISC an
+// otherwise idle lane per map sums the squared seam differences in pair order
+// and stores the RMS per (seam, g, s).  LDS is double-buffered by iteration
+// parity, so one barrier per iteration suffices.
+template <int U, bool PROJECT, bool DISC, bool NOISE, bool NT>
 __global__ __launch_bounds__(kThreads) void k_step_chain(float *__restrict__ state, const float *__restrict__ x0c,
                                                          const float *__restrict__ x0u, StepArgs a, ChainArgs ch,
                                                          float *__restrict__ pre_disc) {
-    __shared__ float s_right[CH + 1][kMaxPairs];  // right-seam copies, slot = tile % (CH + 1)
-    __shared__ float s_left[CH + 1][kMaxPairs];   // left-seam copies
-    __shared__ int16_t s_lidx[kMaxPairs];         // packed index of pair p in the left tile
-    __shared__ int16_t s_ridx[kMaxPairs];         // ... in the right tile
+    static_assert(U <= kThreads - kQuads, "the discrepancy of map u is summed by idle lane kQuads + u");
+    __shared__ float s_right[2][U][kMaxPairs];  // tile k's stepped right-seam values
+    __shared__ float s_left[2][U][kMaxPairs];   // tile k+1's stepped left-seam values
 
     const uint32_t q = threadIdx.x;
     const bool active = q < kQuads;
     const uint32_t b = xcd_remap(blockIdx.x, gridDim.x);
-    const int n_cols = a.G * a.S;
-    const int c = static_cast<int>(b) / n_cols;
-    const int gs = static_cast<int>(b) - c * n_cols;
-    const int g = gs / a.S;
+    const int rg = static_cast<int>(b) / a.blocks_per_rg;
+    const int chunk = static_cast<int>(b) - rg * a.blocks_per_rg;
+    const int r = rg / a.G;
+    const int g = rg - r * a.G;
     const float w = a.w[g];
     const int L = ch.chain_len, O = ch.overlap, NP = ch.n_pairs;
+    const int c = r / L;
+    const int k = r - c * L;
+    const int n_cols = a.G * a.S;
+    const bool owns_seam = k < L - 1;
     const int off = kBeads - O;
 
-    for (int p = q; p < NP; p += kThreads) {
-        int pp = 0;
-        while (block_pair_index(pp + 1, pp + 2, O) <= p && pp + 2 < O) ++pp;
-        const int qq = p - block_pair_index(pp, pp + 1, O) + pp + 1;
-        s_lidx[p] = static_cast<int16_t>(packed_index(off + pp, off + qq));
-        s_ridx[p] = static_cast<int16_t>(packed_index(pp, qq));
-    }
-
-    // Seam membership of this lane's four elements: pair index or -1.
+    // Seam membership of this lane's four elements (pair index or -1), and
+    // whether its 128-byte line (elements 32 m .. 32 m + 31) holds a
+    // left-seam element.  A line spans at most two rows of the map.
     int lp[4], rp[4];
 #pragma unroll
     for (int l = 0; l < 4; ++l) {
@@ -157,85 +172,117 @@ __global__ __launch_bounds__(kThreads) void k_step_chain(float *__restrict__ sta
         lp[l] = (active && j < O) ? block_pair_index(i, j, O) : -1;
         rp[l] = (active && i >= off) ? block_pair_index(i - off, j - off, O) : -1;
     }
-    const bool has_left = lp[0] >= 0 || lp[1] >= 0 || lp[2] >= 0 || lp[3] >= 0;
-    const bool has_right = rp[0] >= 0 || rp[1] >= 0 || rp[2] >= 0 || rp[3] >= 0;
+    bool seam_line = false;
+    if (active) {
+        const int e0 = static_cast<int>(q / 8) * 32, e1 = e0 + 31;
+        int i0, j0, i1, j1;
+        packed_row_col(e0, i0, j0);
+        packed_row_col(e1, i1, j1);
+        // row i0 from column j0 on, row i1 up to column j1: left-seam columns are < O
+        seam_line = (i0 <= O - 2 && j0 < O) || (i1 <= O - 2 && i1 > i0);
+    }
+    const bool right_quad = rp[0] >= 0 || rp[1] >= 0 || rp[2] >= 0 || rp[3] >= 0;
+    const bool left_quad = lp[0] >= 0 || lp[1] >= 0 || lp[2] >= 0 || lp[3] >= 0;
+    // task 0: tile k's quad, or tile k+1's for seam lines of tiles k > 0; task 1: tile 0's halo
+    const bool own = active && !(seam_line && k > 0);
+    const bool halo = seam_line && owns_seam;
+    const bool t0 = own || halo;
+    const bool t0_halo = !own && halo;
+    const bool t1 = own && halo;  // tile 0 only
 
-    // map (tile k) = ((c L + k) G + g) S + s = (c L + k) G S + gs
-    const size_t col_map0 = static_cast<size_t>(c) * L * n_cols + gs;
-    __syncthreads();
+    float4 rc0 = make_float4(0.f, 0.f, 0.f, 0.f), ru0 = rc0, rc1 = rc0, ru1 = rc0;
+    if (t0) {
+        const size_t rr = static_cast<size_t>(r + (t0_halo ? 1 : 0));
+        rc0 = ld4(x0c, rr * kQuads + q);
+        ru0 = ld4(x0u, rr * kQuads + q);
+    }
+    if (t1) {
+        rc1 = ld4(x0c, static_cast<size_t>(r + 1) * kQuads + q);
+        ru1 = ld4(x0u, static_cast<size_t>(r + 1) * kQuads + q);
+    }
+    const size_t off0 = t0_halo ? static_cast<size_t>(n_cols) : 0;  // map offset of task 0
 
-    for (int k0 = 0; k0 < L; k0 += CH) {
-        const int nk = L - k0 < CH ? L - k0 : CH;
-        if (active) {
-            float4 x[CH];
+    const int s0 = chunk * a.maps_per_block;
+    const int s1 = s0 + a.maps_per_block < a.S ? s0 + a.maps_per_block : a.S;
+    const size_t t_base = static_cast<size_t>(rg) * a.S;
+    int par = 0;
+    for (int sb = s0; sb < s1; sb += U, par ^= 1) {
+        const int nu = s1 - sb < U ? s1 - sb : U;
+        float4 y0[U], y1[U];
+        {
+            float4 x0[U], x1[U];
 #pragma unroll
-            for (int u = 0; u < CH; ++u)
-                if (u < nk) x[u] = ld_state<NT>(state, (col_map0 + static_cast<size_t>(k0 + u) * n_cols) * kQuads + q);
+            for (int u = 0; u < U; ++u) {
+                if (u < nu) {
+                    if (t0) x0[u] = ld_state<NT>(state, (t_base + sb + u + off0) * kQuads + q);
+                    if (t1) x1[u] = ld_state<NT>(state, (t_base + sb + u + n_cols) * kQuads + q);
+                }
+            }
 #pragma unroll
-            for (int u = 0; u < CH; ++u) {
-                if (u >= nk) break;
-                const int k = k0 + u;
-                const int reg = c * L + k;
-                const size_t map = col_map0 + static_cast<size_t>(k) * n_cols;
-                const float4 xc = ld4(x0c, static_cast<size_t>(reg) * kQuads + q);
-                const float4 xu = ld4(x0u, static_cast<size_t>(reg) * kQuads + q);
-                const float4 z = NOISE ? philox_normals(q, static_cast<uint32_t>(map), a.slot, a.k0, a.k1)
-                                       : make_float4(0.f, 0.f, 0.f, 0.f);
-                const float4 y = step4(x[u], xc, xu, w, a.c, z);
-                const bool lft = has_left && k > 0;
-                const bool rgt = has_right && k < L - 1;
-                if (!lft && !rgt) {
-                    st_state<NT>(state, map * kQuads + q, y);
-                } else {
-                    const float v[4] = {y.x, y.y, y.z, y.w};
-                    const int slot = k % (CH + 1);
-                    float *dst = state + map * kPacked + 4 * q;
-#pragma unroll
-                    for (int l = 0; l < 4; ++l) {
-                        const bool in_l = lft && lp[l] >= 0;
-                        const bool in_r = rgt && rp[l] >= 0;
-                        if (in_l) s_left[slot][lp[l]] = v[l];
-                        if (in_r) s_right[slot][rp[l]] = v[l];
-                        if (!in_l && !in_r) dst[l] = v[l];
-                    }
+            for (int u = 0; u < U; ++u) {
+                if (u >= nu) break;
+                const size_t map = t_base + sb + u;
+                if (t0) {
+                    const uint32_t m0 = static_cast<uint32_t>(map + off0);
+                    const float4 z = NOISE ? philox_normals(q, m0, a.slot, a.k0, a.k1)
+                                           : make_float4(0.f, 0.f, 0.f, 0.f);
+                    y0[u] = step4(x0[u], rc0, ru0, w, a.c, z);
+                }
+                if (t1) {
+                    const uint32_t m1 = static_cast<uint32_t>(map + n_cols);
+                    const float4 z = NOISE ? philox_normals(q, m1, a.slot, a.k0, a.k1)
+                                           : make_float4(0.f, 0.f, 0.f, 0.f);
+                    y1[u] = step4(x1[u], rc1, ru1, w, a.c, z);
+                }
+                // right-seam values of tile k (task 0 of own lanes)
+                if (own && owns_seam && right_quad) {
+                    if (rp[0] >= 0) s_right[par][u][rp[0]] = y0[u].x;
+                    if (rp[1] >= 0) s_right[par][u][rp[1]] = y0[u].y;
+                    if (rp[2] >= 0) s_right[par][u][rp[2]] = y0[u].z;
+                    if (rp[3] >= 0) s_right[par][u][rp[3]] = y0[u].w;
+                }
+                // left-seam values of tile k+1 (task 0 of halo lanes, task 1 in tile 0)
+                if (halo && left_quad) {
+                    const float4 h = t1 ? y1[u] : y0[u];
+                    if (lp[0] >= 0) s_left[par][u][lp[0]] = h.x;
+                    if (lp[1] >= 0) s_left[par][u][lp[1]] = h.y;
+                    if (lp[2] >= 0) s_left[par][u][lp[2]] = h.z;
+                    if (lp[3] >= 0) s_left[par][u][lp[3]] = h.w;
                 }
             }
         }
-        __syncthreads();
-        // Seams j = jlo .. jhi join tiles j and j+1, both stepped by now.
-        const int jlo = k0 > 0 ? k0 - 1 : 0;
-        const int jhi = k0 + nk - 2;
-        const int n_seams = jhi - jlo + 1;
-        if (n_seams > 0) {
-            for (int it = q; it < n_seams * NP; it += kThreads) {
-                const int j = jlo + it / NP;
-                const int p = it - (j - jlo) * NP;
-                const float lv = s_right[j % (CH + 1)][p];      // copy in the left tile
-                const float rv = s_left[(j + 1) % (CH + 1)][p];  // copy in the right tile
-                const size_t map_l = col_map0 + static_cast<size_t>(j) * n_cols;
-                const size_t map_r = map_l + n_cols;
-                if (PROJECT) {
-                    const float m = (lv + rv) * 0.5f;
-                    state[map_l * kPacked + s_lidx[p]] = m;
-                    state[map_r * kPacked + s_ridx[p]] = m;
-                } else {
-                    state[map_l * kPacked + s_lidx[p]] = lv;
-                    state[map_r * kPacked + s_ridx[p]] = rv;
+        if (owns_seam) __syncthreads();
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (u >= nu) break;
+            const size_t map = t_base + sb + u;
+            if (PROJECT && owns_seam) {
+                if (own && right_quad) {  // left copy (tile k) + right copy (tile k+1)
+                    if (rp[0] >= 0) y0[u].x = (y0[u].x + s_left[par][u][rp[0]]) * 0.5f;
+                    if (rp[1] >= 0) y0[u].y = (y0[u].y + s_left[par][u][rp[1]]) * 0.5f;
+                    if (rp[2] >= 0) y0[u].z = (y0[u].z + s_left[par][u][rp[2]]) * 0.5f;
+                    if (rp[3] >= 0) y0[u].w = (y0[u].w + s_left[par][u][rp[3]]) * 0.5f;
+                }
+                if (halo && left_quad) {
+                    float4 &h = t1 ? y1[u] : y0[u];
+                    if (lp[0] >= 0) h.x = (s_right[par][u][lp[0]] + h.x) * 0.5f;
+                    if (lp[1] >= 0) h.y = (s_right[par][u][lp[1]] + h.y) * 0.5f;
+                    if (lp[2] >= 0) h.z = (s_right[par][u][lp[2]] + h.z) * 0.5f;
+                    if (lp[3] >= 0) h.w = (s_right[par][u][lp[3]] + h.w) * 0.5f;
                 }
             }
-            if (DISC && static_cast<int>(q) < n_seams) {
-                const int j = jlo + static_cast<int>(q);
-                const float *lv = s_right[j % (CH + 1)];
-                const float *rv = s_left[(j + 1) % (CH + 1)];
+            if (t0) st_state<NT>(state, (map + off0) * kQuads + q, y0[u]);
+            if (t1) st_state<NT>(state, (map + n_cols) * kQuads + q, y1[u]);
+            if (DISC && owns_seam && static_cast<int>(q) == kQuads + u) {  // an otherwise idle lane
                 float acc = 0.f;
                 for (int p = 0; p < NP; ++p) {
-                    const float d = lv[p] - rv[p];
+                    const float d = s_right[par][u][p] - s_left[par][u][p];
                     acc = fmaf(d, d, acc);
                 }
-                pre_disc[static_cast<size_t>(c * (L - 1) + j) * n_cols + gs] = sqrtf(acc / static_cast<float>(NP));
+                pre_disc[(static_cast<size_t>(c) * (L - 1) + k) * n_cols + static_cast<size_t>(g) * a.S + sb + u] =
+                    sqrtf(acc / static_cast<float>(NP));
             }
         }
-        __syncthreads();
     }
 }
 
@@ -281,12 +328,16 @@ hipError_t launch_step_indep(float *state, const float *x0c, const float *x0u, S
 hipError_t launch_step_chain(float *state, const float *x0c, const float *x0u, StepArgs a, ChainArgs ch,
                              bool project, float *pre_disc, bool noise, hipStream_t stream) {
     const int64_t n_maps = static_cast<int64_t>(a.R) * a.G * a.S;
-    const int64_t blocks = static_cast<int64_t>(a.R / ch.chain_len) * a.G * a.S;
+    int64_t mpb = (n_maps / kChainGrid) & ~int64_t(1);
+    mpb = mpb < kChainMapsMin ? kChainMapsMin : (mpb > kChainMapsMax ? kChainMapsMax : mpb);
+    a.maps_per_block = static_cast<int32_t>(mpb);
+    a.blocks_per_rg = (a.S + a.maps_per_block - 1) / a.maps_per_block;
+    const int64_t blocks = static_cast<int64_t>(a.R) * a.G * a.blocks_per_rg;
     const dim3 grid(static_cast<uint32_t>(blocks));
     const bool disc = pre_disc != nullptr;
     const bool nt = static_cast<size_t>(n_maps) * kPacked * 4 > kStreamBytes;
-#define PC_CHAIN(P, D, N, T)                                                                                    \
-    hipLaunchKernelGGL((k_step_chain<kChainCh, P, D, N, T>), grid, dim3(kThreads), 0, stream, state, x0c, x0u, a, \
+#define PC_CHAIN(P, D, N, T)                                                                                     \
+    hipLaunchKernelGGL((k_step_chain<kChainU, P, D, N, T>), grid, dim3(kThreads), 0, stream, state, x0c, x0u, a, \
                        ch, pre_disc)
 #define PC_CHAIN_NT(P, D, N) \
     if (nt) PC_CHAIN(P, D, N, true); else PC_CHAIN(P, D, N, false)
