@@ -5,12 +5,14 @@
 //      gathers row i of A = D o D into 64 VGPRs.
 //   2. Double centring B = J A J (times -1/2) from the row means (LDS) and the
 //      grand mean (wavefront reduction); row i of B stays in VGPRs.
-//   3. Block-4 subspace iteration with Rayleigh-Ritz: Z = B Q (Q broadcast
-//      from LDS, 256 FMAs per lane), H = Q^T Z by wavefront reductions, a 4x4
-//      Jacobi eigensolve (wave-uniform), Ritz vectors V = Q W, Y = Z W = B V,
-//      residuals ||Y_k - theta_k V_k||, and Q <- orth(Y) by modified
-//      Gram-Schmidt.  Stops when the residuals of the three largest Ritz pairs
-//      reach the float32 floor or after max_iters.
+//   3. Block-4 subspace iteration with Rayleigh-Ritz: Q <- orth(Z) by
+//      modified Gram-Schmidt, Z = B Q (Q broadcast from LDS, 256 FMAs per
+//      lane), H = Q^T Z by DPP wavefront reductions, a 4x4 Jacobi eigensolve
+//      (wave-uniform), Ritz vectors V = Q W, Z W = B V and the residuals
+//      ||B V_k - theta_k V_k|| of the three largest.  Stops when those reach
+//      the float32 floor or after max_iters Rayleigh-Ritz steps.  The
+//      workgroup is capped at 128 VGPRs so four maps run per SIMD (the kernel
+//      is VALU-bound; four waves beat three by 12% on MI355X).
 //   4. The iteration finds the eigenvalues of largest magnitude.  If a
 //      negative one could hide a positive eigenvalue (the third largest Ritz
 //      value is below the smallest magnitude found), it reruns on B + mu I
@@ -26,10 +28,24 @@ namespace {
 constexpr int kLanes = 64;
 constexpr int kBlk = 4;
 
+// Wavefront sum by DPP: quad permutes, then the half-row and row mirrors
+// leave every lane of a 16-lane row holding the row total (each step adds a
+// value to its mirror image, so the lanes of a row round identically); row
+// broadcasts 15 and 31 fold the four rows into lane 63, which is read back
+// as a wave-uniform value.  Six full-rate DPP adds and one readlane, in a
+// fixed order.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
+    v += dpp<0xB1>(v);         // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);         // quad_perm [2,3,0,1]
+    v += dpp<0x141>(v);        // row_half_mirror
+    v += dpp<0x140>(v);        // row_mirror
+    v += dpp<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+    v += dpp<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // Fixed pseudo-random start vectors (an integer hash of (bead, column)).
@@ -43,54 +59,58 @@ __device__ __forceinline__ float start_vec(int i, int k) {
     return static_cast<float>(x >> 8) * 0x1p-23f - 1.0f;
 }
 
-// Cyclic Jacobi on a symmetric 4x4 (values identical in every lane).
-// On return h is diagonal to float32 precision and w holds the eigenvectors
-// as columns.
+// Cyclic Jacobi on a symmetric 4x4 (values identical in every lane).  The
+// rotation that zeroes h_pq uses t = sgn(th) / (|th| + sqrt(th^2 + 1)) with
+// th = (h_qq - h_pp) / (2 h_pq), c = 1 / sqrt(1 + t^2), s = t c; only the
+// entries it changes are updated (h_pp -= t h_pq, h_qq += t h_pq, rows r != p,
+// q rotate).  t needs no correct rounding: c and s are formed from it, so the
+// rotation stays orthogonal, and the hardware rcp / rsq / sqrt are used.  On
+// return h is diagonal to float32 precision and w holds the eigenvectors as
+// columns.
+template <int P, int Q>
+__device__ __forceinline__ void jacobi_rotate(float (&h)[kBlk][kBlk], float (&w)[kBlk][kBlk]) {
+    const float apq = h[P][Q];
+    if (apq == 0.f) return;
+    const float th = (h[Q][Q] - h[P][P]) * 0.5f * __builtin_amdgcn_rcpf(apq);
+    const float at = fabsf(th);
+    const float t = at > 1e18f ? 0.5f * __builtin_amdgcn_rcpf(th)
+                               : copysignf(__builtin_amdgcn_rcpf(at + __builtin_amdgcn_sqrtf(fmaf(th, th, 1.f))), th);
+    const float c = __builtin_amdgcn_rsqf(fmaf(t, t, 1.f));
+    const float sn = t * c;
+    h[P][P] = fmaf(-t, apq, h[P][P]);
+    h[Q][Q] = fmaf(t, apq, h[Q][Q]);
+    h[P][Q] = h[Q][P] = 0.f;
+#pragma unroll
+    for (int r = 0; r < kBlk; ++r) {
+        if (r == P || r == Q) continue;
+        const float hp = h[r][P], hq = h[r][Q];
+        h[r][P] = h[P][r] = c * hp - sn * hq;
+        h[r][Q] = h[Q][r] = sn * hp + c * hq;
+    }
+#pragma unroll
+    for (int r = 0; r < kBlk; ++r) {
+        const float wp = w[r][P], wq = w[r][Q];
+        w[r][P] = c * wp - sn * wq;
+        w[r][Q] = sn * wp + c * wq;
+    }
+}
+
 __device__ __forceinline__ void jacobi4(float (&h)[kBlk][kBlk], float (&w)[kBlk][kBlk]) {
 #pragma unroll
     for (int r = 0; r < kBlk; ++r)
 #pragma unroll
         for (int c = 0; c < kBlk; ++c) w[r][c] = r == c ? 1.f : 0.f;
     for (int sweep = 0; sweep < 8; ++sweep) {
-        float off = 0.f, dia = 0.f;
-#pragma unroll
-        for (int r = 0; r < kBlk; ++r) {
-            dia += h[r][r] * h[r][r];
-#pragma unroll
-            for (int c = r + 1; c < kBlk; ++c) off += h[r][c] * h[r][c];
-        }
-        if (off <= 1e-14f * dia || off == 0.f) break;
-#pragma unroll
-        for (int p = 0; p < kBlk - 1; ++p) {
-#pragma unroll
-            for (int q = p + 1; q < kBlk; ++q) {
-                const float apq = h[p][q];
-                if (apq == 0.f) continue;
-                const float theta = (h[q][q] - h[p][p]) / (2.f * apq);
-                const float at = fabsf(theta);
-                const float t = at > 1e18f ? 0.5f / theta : copysignf(1.f, theta) / (at + sqrtf(theta * theta + 1.f));
-                const float c = 1.f / sqrtf(t * t + 1.f);
-                const float s = t * c;
-#pragma unroll
-                for (int r = 0; r < kBlk; ++r) {
-                    const float hp = h[r][p], hq = h[r][q];
-                    h[r][p] = c * hp - s * hq;
-                    h[r][q] = s * hp + c * hq;
-                }
-#pragma unroll
-                for (int r = 0; r < kBlk; ++r) {
-                    const float hp = h[p][r], hq = h[q][r];
-                    h[p][r] = c * hp - s * hq;
-                    h[q][r] = s * hp + c * hq;
-                }
-#pragma unroll
-                for (int r = 0; r < kBlk; ++r) {
-                    const float wp = w[r][p], wq = w[r][q];
-                    w[r][p] = c * wp - s * wq;
-                    w[r][q] = s * wp + c * wq;
-                }
-            }
-        }
+        const float off = h[0][1] * h[0][1] + h[0][2] * h[0][2] + h[0][3] * h[0][3] + h[1][2] * h[1][2] +
+                          h[1][3] * h[1][3] + h[2][3] * h[2][3];
+        const float dia = h[0][0] * h[0][0] + h[1][1] * h[1][1] + h[2][2] * h[2][2] + h[3][3] * h[3][3];
+        if (off <= 1e-14f * dia) break;
+        jacobi_rotate<0, 1>(h, w);
+        jacobi_rotate<0, 2>(h, w);
+        jacobi_rotate<0, 3>(h, w);
+        jacobi_rotate<1, 2>(h, w);
+        jacobi_rotate<1, 3>(h, w);
+        jacobi_rotate<2, 3>(h, w);
     }
 }
 
@@ -105,7 +125,7 @@ __device__ __forceinline__ void orthonormalise(int lane, const float (&y)[kBlk],
             for (int l = 0; l < k; ++l) v -= wave_sum(q[l] * v) * q[l];
             const float n2 = wave_sum(v * v);
             if (n2 > 1e-30f) {
-                v *= 1.f / sqrtf(n2);
+                v *= __builtin_amdgcn_rsqf(n2);
                 break;
             }
             v = start_vec(lane, k);
@@ -115,41 +135,52 @@ __device__ __forceinline__ void orthonormalise(int lane, const float (&y)[kBlk],
     }
 }
 
-// Block-4 subspace iteration with Rayleigh-Ritz on B + mu I.  On return
-// theta (descending, shift included) and vec (lane = bead) hold the Ritz
-// pairs; the result is the smallest Ritz magnitude found.
+// z = (B + mu I) q for the four per-lane columns q (row `lane` of B in b).
+__device__ __forceinline__ void block_matvec(const float (&b)[kBeads], float mu, int lane, const float (&q)[kBlk],
+                                             float4 *s_q, float (&z)[kBlk]) {
+    s_q[lane] = make_float4(q[0], q[1], q[2], q[3]);
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kBlk; ++k) z[k] = mu * q[k];
+#pragma unroll
+    for (int j = 0; j < kBeads; ++j) {
+        const float4 qj = s_q[j];
+        z[0] = fmaf(b[j], qj.x, z[0]);
+        z[1] = fmaf(b[j], qj.y, z[1]);
+        z[2] = fmaf(b[j], qj.z, z[2]);
+        z[3] = fmaf(b[j], qj.w, z[3]);
+        // keep at most 8 broadcast rows of Q in flight (otherwise all 64
+        // LDS reads are hoisted and the register file overflows)
+        if (j % 8 == 7) __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+}
+
+// Block-4 subspace iteration on B + mu I.  Each iteration orthonormalises
+// the last product (q <- MGS(z), starting from fixed pseudo-random vectors),
+// multiplies again (z <- (B + mu I) q), and from the second product on tests
+// the Rayleigh-Ritz pairs of (q, z): H = q^T z, H = W diag(theta) W^T,
+// vec = q W, residual ||z W - theta vec|| of the three largest.  On return
+// theta (descending, shift included) and vec (lane = bead) hold the last Ritz
+// pairs; the result is the smallest Ritz magnitude.
 __device__ __forceinline__ float subspace(const float (&b)[kBeads], float mu, int32_t max_iters, int lane,
                                           float4 *s_q, float (&theta)[kBlk], float (&vec)[kBlk]) {
-    float q[kBlk];
-    {
-        float y0[kBlk];
+    float q[kBlk], z[kBlk];
 #pragma unroll
-        for (int k = 0; k < kBlk; ++k) y0[k] = start_vec(lane, k);
-        orthonormalise(lane, y0, q);
-    }
+    for (int k = 0; k < kBlk; ++k) z[k] = start_vec(lane, k);
     float rho = 0.f;
-    for (int it = 0; it < max_iters; ++it) {
-        s_q[lane] = make_float4(q[0], q[1], q[2], q[3]);
-        __syncthreads();
-        float z[kBlk] = {mu * q[0], mu * q[1], mu * q[2], mu * q[3]};
-#pragma unroll
-        for (int j = 0; j < kBeads; ++j) {
-            const float4 qj = s_q[j];
-            z[0] = fmaf(b[j], qj.x, z[0]);
-            z[1] = fmaf(b[j], qj.y, z[1]);
-            z[2] = fmaf(b[j], qj.z, z[2]);
-            z[3] = fmaf(b[j], qj.w, z[3]);
-        }
-        __syncthreads();
-        // H = Q^T (B + mu I) Q, symmetrised.
+    for (int it = 0; it <= max_iters; ++it) {
+        orthonormalise(lane, z, q);
+        block_matvec(b, mu, lane, q, s_q, z);
+        if (it == 0) continue;  // the first product only seeds the subspace
         float h[kBlk][kBlk], w[kBlk][kBlk];
 #pragma unroll
         for (int r = 0; r < kBlk; ++r)
 #pragma unroll
             for (int c = r; c < kBlk; ++c) {
-                const float s = wave_sum(q[r] * z[c] + q[c] * z[r]) * 0.5f;
-                h[r][c] = s;
-                h[c][r] = s;
+                const float sm = wave_sum(q[r] * z[c] + q[c] * z[r]) * 0.5f;
+                h[r][c] = sm;
+                h[c][r] = sm;
             }
         jacobi4(h, w);
         float d[kBlk] = {h[0][0], h[1][1], h[2][2], h[3][3]};
@@ -181,19 +212,20 @@ __device__ __forceinline__ float subspace(const float (&b)[kBeads], float mu, in
             rho = fminf(rho, fabsf(d[k]));
         }
         const float tol = 4e-6f * thmax;
-        bool done = it >= 1;
+        bool done = true;
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
             const float r = yv[k] - d[k] * vec[k];
             done = done && wave_sum(r * r) <= tol * tol;
         }
         if (done) break;
-        orthonormalise(lane, yv, q);
+#pragma unroll
+        for (int k = 0; k < kBlk; ++k) z[k] = yv[k];
     }
     return rho;
 }
 
-__global__ __launch_bounds__(kLanes) void k_mds(const float *__restrict__ maps, float *__restrict__ coords,
+__global__ __launch_bounds__(kLanes, 4) void k_mds(const float *__restrict__ maps, float *__restrict__ coords,
                                                 float *__restrict__ eigvals, int32_t max_iters) {
     __shared__ float4 s_map[kQuads];
     __shared__ float4 s_q[kBeads];
