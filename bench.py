@@ -41,6 +41,9 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target duration of the oracle baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--eps-buffers", action="store_true",
+                   help="step with noise predictions read from buffers (the interface of a trained denoiser) "
+                        "instead of the point-mass stand-in: 16 B per element-step instead of 8")
     p.add_argument("--copy-only", action="store_true",
                    help="time a plain device-to-device copy of the workload's state size instead "
                         "(the calibration kernel for the HBM byte counters)")
@@ -159,13 +162,24 @@ def main():
     coords = torch.empty(lay.n_maps * 64 * 3, dtype=torch.float32, device=dev)
     project = 1 if wl.chain_len > 1 else 0
     stream = torch.cuda.current_stream(dev)
+    if args.eps_buffers:
+        # stand-ins for a network's per-map outputs, drawn once; each step reads both
+        gen = torch.Generator(device=dev).manual_seed(args.seed)
+        eps_c = torch.randn(lay.n_maps * pc.PACKED, generator=gen, device=dev)
+        eps_u = torch.randn(lay.n_maps * pc.PACKED, generator=gen, device=dev)
+        a_t, a_n = pc.pc_ddim_schedule(n_steps)
 
     def one_pass(events=None):
         pc.pc_init_state(state, lay, args.seed)
         if events:
             events[0].record(stream)
-        pc.pc_ddim_sample(state, x0c_d, x0u_d, list(wl.w), lay, n_steps, wl.eta, args.seed,
-                          project_every=project, init=False)
+        if args.eps_buffers:
+            for i in range(n_steps):
+                pc.pc_ddim_cfg_step_eps(state, eps_c, eps_u, list(wl.w), lay, a_t[i], a_n[i], wl.eta, args.seed,
+                                        i + 1, project_seams=bool(project))
+        else:
+            pc.pc_ddim_sample(state, x0c_d, x0u_d, list(wl.w), lay, n_steps, wl.eta, args.seed,
+                              project_every=project, init=False)
         if events:
             events[1].record(stream)
         pc.pc_mds_recover(state, coords)
@@ -188,10 +202,13 @@ def main():
     step_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     mds_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     launch_ms = step_ms / n_steps
-    bytes_per_launch = lay.n_maps * STEP_BYTES_PER_MAP + lay.n_regions * REF_BYTES_PER_REGION
+    if args.eps_buffers:
+        bytes_per_launch = lay.n_maps * STEP_BYTES_PER_MAP * 2   # + both noise predictions read
+    else:
+        bytes_per_launch = lay.n_maps * STEP_BYTES_PER_MAP + lay.n_regions * REF_BYTES_PER_REGION
     achieved = bytes_per_launch / (launch_ms * 1e-3) / 1e9
     traj_steps = lay.n_maps * n_steps
-    traffic, traffic_kernel = measured_traffic(wl.name)
+    traffic, traffic_kernel = measured_traffic(wl.name) if not args.eps_buffers else (None, None)
 
     out = {
         "metric": "DDIM trajectory-steps/s (64-bead maps) + % HBM peak; MDS maps/s",
@@ -203,7 +220,8 @@ def main():
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": wl.name, "maps": lay.n_maps, "regions": wl.n_regions, "guidance": wl.n_guidance,
                    "trajectories": wl.n_traj, "chain_len": wl.chain_len, "ddim_steps": n_steps, "eta": wl.eta,
-                   "seed": args.seed, "parallelism": "single GPU"},
+                   "seed": args.seed, "denoiser": "noise-prediction buffers" if args.eps_buffers else "point-mass",
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "k_step_indep" if wl.chain_len == 1 else "k_step_chain",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "traffic_unit": "bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-scaled)",

@@ -97,6 +97,19 @@ PC_API pc_status pc_ddim_schedule(int32_t n_steps, int32_t T, double beta_start,
                            double *abar_t, double *abar_next);
 
 /*
+ * Cosine noise schedule (host), the schedule of ChromoGen's sampler
+ * (section 4.3.2), in the form of Nichol & Dhariwal (ICML 2021): with
+ * f(u) = cos^2(pi/2 (u + s)/(1 + s)), beta_t = min(1 - f((t+1)/T) / f(t/T),
+ * beta_max) and abar_t = prod_{u <= t} (1 - beta_u); the DDIM grid and
+ * outputs are those of pc_ddim_schedule (s = 0.008, beta_max = 0.999 are the
+ * published values).
+ * Errors: NULL outputs; T < 2; n_steps < 1 or not dividing T; s outside
+ * [0, 1) or beta_max outside (0, 1).
+ */
+PC_API pc_status pc_ddim_schedule_cosine(int32_t n_steps, int32_t T, double s, double beta_max, double *abar_t,
+                                         double *abar_next);
+
+/*
  * Initial state x_T: an independent N(0, 1) draw per packed entry of every
  * map, Philox slot 0 (each region starts from independent Gaussian noise,
  * section 4.3.1).
@@ -134,6 +147,24 @@ PC_API pc_status pc_ddim_cfg_step(float *state, const float *x0_cond, const floa
                            const pc_layout *layout, double abar_t, double abar_next, double eta,
                            uint64_t seed, uint32_t slot, int32_t project_seams, float *pre_disc,
                            void *stream);
+
+/*
+ * The same guided DDIM step, projection and discrepancy as
+ * pc_ddim_cfg_step, for a real denoiser: the conditional and unconditional
+ * noise predictions of every map come from buffers (what the conditional
+ * U-Net returns for the current state, section 3.1) instead of the
+ * point-mass stand-in.  eps = eps_u + w_g (eps_c - eps_u), then the DDIM
+ * update as above.  Algorithmic traffic: 16 B per element (state read and
+ * written, both predictions read).  With eta = 1 on a stride-1 grid this is
+ * the DDPM ancestral p-sample of the pages' spatial runs (section 5.1).
+ *   eps_cond,
+ *   eps_uncond  device float [R][G][S][2016], read.
+ * Other arguments and errors as pc_ddim_cfg_step (references are not used).
+ */
+PC_API pc_status pc_ddim_cfg_step_eps(float *state, const float *eps_cond, const float *eps_uncond, const float *w,
+                                      const pc_layout *layout, double abar_t, double abar_next, double eta,
+                                      uint64_t seed, uint32_t slot, int32_t project_seams, float *pre_disc,
+                                      void *stream);
 
 /*
  * The whole reverse chain on the stream: optionally x_T (pc_init_state), then

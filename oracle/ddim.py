@@ -48,6 +48,13 @@ def ddim_update(x, eps, a: float, a_next: float, sigma: float, z):
     return out
 
 
+def ddim_cfg_step_eps(x, eps_c, eps_u, w, a: float, a_next: float, eta: float, z):
+    """The same step when the conditional and unconditional noise predictions come
+    from a network (buffers), not from the point-mass stand-in."""
+    eps = cfg_combine(eps_c, eps_u, w)
+    return ddim_update(x, eps, a, a_next, ddim_sigma(a, a_next, eta), z)
+
+
 def ddim_cfg_step(x, x0c, x0u, w, a: float, a_next: float, eta: float, z):
     """One fused guidance + DDIM step.  ``w`` broadcasts against ``x``."""
     eps_c = eps_point_mass(x, x0c, a)

@@ -14,6 +14,12 @@ target is the clean sample, abar = 1.
 
 DDIM noise scale for a step from abar a to abar a':
     sigma(eta) = eta * sqrt((1 - a') / (1 - a)) * sqrt(1 - a / a').
+
+Cosine schedule (Nichol & Dhariwal, "Improved denoising diffusion
+probabilistic models", ICML 2021), the schedule ChromoGen's sampler uses
+(ParaChromo, section 4.3.2): with f(u) = cos^2(pi/2 (u + s)/(1 + s)),
+beta_t = min(1 - f((t+1)/T) / f(t/T), beta_max) and abar_t the running
+product of (1 - beta_t), as for the linear schedule.
 """
 
 from __future__ import annotations
@@ -39,6 +45,21 @@ def alpha_bar(T: int = 1000, beta_start: float = 1e-4, beta_end: float = 0.02) -
     return out
 
 
+def betas_cosine(T: int = 1000, s: float = 0.008, beta_max: float = 0.999) -> np.ndarray:
+    def f(u):
+        return math.cos((u + s) / (1.0 + s) * math.pi / 2.0) ** 2
+    return np.array([min(1.0 - f((t + 1) / T) / f(t / T), beta_max) for t in range(T)], dtype=np.float64)
+
+
+def alpha_bar_from_betas(b) -> np.ndarray:
+    out = np.empty(len(b), dtype=np.float64)
+    acc = 1.0
+    for t in range(len(b)):
+        acc *= 1.0 - b[t]
+        out[t] = acc
+    return out
+
+
 def ddim_timesteps(n_steps: int, T: int = 1000) -> np.ndarray:
     if n_steps < 1 or T % n_steps:
         raise ValueError("n_steps must divide T")
@@ -46,9 +67,11 @@ def ddim_timesteps(n_steps: int, T: int = 1000) -> np.ndarray:
     return np.array([T - d * (i + 1) for i in range(n_steps)], dtype=np.int64)
 
 
-def ddim_pairs(n_steps: int, T: int = 1000, beta_start: float = 1e-4, beta_end: float = 0.02):
-    """[(a_i, a'_i)] for each DDIM step i: abar before and after the step."""
-    ab = alpha_bar(T, beta_start, beta_end)
+def ddim_pairs(n_steps: int, T: int = 1000, beta_start: float = 1e-4, beta_end: float = 0.02, ab=None):
+    """[(a_i, a'_i)] for each DDIM step i: abar before and after the step.  ``ab`` overrides the
+    linear schedule with any abar table of length T."""
+    if ab is None:
+        ab = alpha_bar(T, beta_start, beta_end)
     tau = ddim_timesteps(n_steps, T)
     out = []
     for i in range(n_steps):

@@ -57,6 +57,17 @@ def test_schedule_matches_oracle_bitwise():
         pc.pc_ddim_schedule(3)
 
 
+def test_cosine_schedule_matches_oracle():
+    ab = schedule.alpha_bar_from_betas(schedule.betas_cosine())
+    for n in (50, 1000):
+        a, b = pc.pc_ddim_schedule_cosine(n)
+        want = schedule.ddim_pairs(n, ab=ab)
+        assert np.allclose(a, [p[0] for p in want], rtol=1e-14, atol=0)
+        assert np.allclose(b, [p[1] for p in want], rtol=1e-14, atol=0)
+    with pytest.raises(pc.PCError):
+        pc.pc_ddim_schedule_cosine(50, s=-0.1)
+
+
 def test_seam_index_map_matches_oracle():
     for o in (2, 5, 12, 32):
         li, ri = seam.seam_pairs(o)
@@ -114,6 +125,10 @@ def test_step_validation(lib, args, status):
 
 def test_other_validation(lib):
     lay = _lay()
+    assert lib.pc_ddim_cfg_step_eps(FAKE, None, FAKE, W, ctypes.byref(lay), 0.3, 0.5, 1.0, 0, 1, 0, None, None) == -1
+    assert lib.pc_ddim_cfg_step_eps(FAKE, FAKE, ctypes.c_void_p(4104), W, ctypes.byref(lay), 0.3, 0.5, 1.0, 0, 1, 0,
+                                    None, None) == -3
+    assert lib.pc_ddim_cfg_step_eps(FAKE, FAKE, FAKE, W, ctypes.byref(lay), 0.6, 0.5, 1.0, 0, 1, 0, None, None) == -4
     assert lib.pc_seam_project(FAKE, ctypes.byref(lay), None) == -2          # no chains
     assert lib.pc_seam_discrepancy(FAKE, ctypes.byref(lay), FAKE, None, None) == -2
     assert lib.pc_mds_recover(FAKE, -1, FAKE, None, 0, None) == -2

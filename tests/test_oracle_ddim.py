@@ -149,3 +149,42 @@ def test_eta1_standardised_residual_statistics():
             r = (rho - m).reshape(-1)
             assert abs(r.mean()) < 5.0 / math.sqrt(r.size)
             assert abs(r.var() - 1.0) < 0.01
+
+
+def test_cosine_schedule_telescopes():
+    # without clipping, prod_{i<=t} (1 - beta_i) = prod f(i+1)/f(i) = f(t+1)/f(0)
+    b = schedule.betas_cosine()
+    ab = schedule.alpha_bar_from_betas(b)
+
+    def f(u):
+        return math.cos((u + 0.008) / 1.008 * math.pi / 2) ** 2
+
+    clipped = np.nonzero(b >= 0.999)[0]
+    first_clip = clipped[0] if clipped.size else len(b)
+    assert first_clip >= 990   # only the very end of the schedule is clipped
+    for t in (0, 1, 100, 500, 900, first_clip - 1):
+        assert ab[t] == pytest.approx(f((t + 1) / 1000) / f(0.0), rel=1e-12)
+    assert np.all(np.diff(ab) < 0) and np.all(b <= 0.999)
+    pairs = schedule.ddim_pairs(50, ab=ab)
+    assert pairs[0][0] == ab[980] and pairs[-1] == (ab[0], 1.0)
+
+
+def test_eps_buffer_step():
+    rng = np.random.default_rng(4)
+    x0 = rng.uniform(1, 20, 2016)
+    eps = rng.standard_normal(2016)
+    a, an = AB[700], AB[680]
+    x = math.sqrt(a) * x0 + math.sqrt(1 - a) * eps
+    # true noise on both branches: x0_hat = x0 exactly, so the step is the closed form below
+    for eta in (0.0, 1.0):
+        z = rng.standard_normal(2016)
+        sig = schedule.ddim_sigma(a, an, eta)
+        want = math.sqrt(an) * x0 + math.sqrt(1 - an - sig * sig) * eps + sig * z
+        got = ddim.ddim_cfg_step_eps(x, eps, eps + 3.0, 1.0, a, an, eta, z)   # w = 1 ignores eps_u
+        assert np.allclose(got, want, rtol=0, atol=1e-10)
+    # point-mass predictions as buffers reproduce the stand-in step
+    x0c, x0u = rng.uniform(1, 20, (2, 2016))
+    ec, eu = ddim.eps_point_mass(x, x0c, a), ddim.eps_point_mass(x, x0u, a)
+    z = rng.standard_normal(2016)
+    assert np.allclose(ddim.ddim_cfg_step_eps(x, ec, eu, 0.3, a, an, 1.0, z),
+                       ddim.ddim_cfg_step(x, x0c, x0u, 0.3, a, an, 1.0, z), rtol=0, atol=1e-12)

@@ -16,7 +16,7 @@ import numpy as np
 from . import _lib
 
 __all__ = ["PCError", "PCLayout", "PACKED", "BEADS", "pc_version", "pc_last_error", "pc_ddim_schedule",
-           "pc_init_state", "pc_ddim_cfg_step", "pc_ddim_sample", "pc_seam_project", "pc_seam_discrepancy",
+           "pc_ddim_schedule_cosine", "pc_init_state", "pc_ddim_cfg_step", "pc_ddim_cfg_step_eps", "pc_ddim_sample", "pc_seam_project", "pc_seam_discrepancy",
            "pc_mds_recover", "pc_philox_block", "pc_philox_fill", "pc_normal_fill", "pc_seam_index_map"]
 
 BEADS = 64
@@ -101,6 +101,16 @@ def pc_ddim_schedule(n_steps: int, T: int = 1000, beta_start: float = 1e-4, beta
     return a, b
 
 
+def pc_ddim_schedule_cosine(n_steps: int, T: int = 1000, s: float = 0.008, beta_max: float = 0.999):
+    """(abar_t, abar_next) of the cosine schedule: float64 numpy arrays [n_steps]."""
+    a = np.zeros(n_steps, dtype=np.float64)
+    b = np.zeros(n_steps, dtype=np.float64)
+    st = _lib.load().pc_ddim_schedule_cosine(n_steps, T, s, beta_max, a.ctypes.data_as(_lib.c_double_p),
+                                             b.ctypes.data_as(_lib.c_double_p))
+    _check(st, "pc_ddim_schedule_cosine")
+    return a, b
+
+
 def pc_init_state(state, layout: PCLayout, seed: int) -> None:
     t = _torch()
     lay = layout.c()
@@ -125,6 +135,19 @@ def pc_ddim_cfg_step(state, x0_cond, x0_uncond, w, layout: PCLayout, abar_t: flo
         float(abar_t), float(abar_next), float(eta), seed, slot, int(bool(project_seams)),
         _dev(pre_disc, t.float32, layout.n_seams * layout.n_guidance * layout.n_traj, "pre_disc"),
         _stream(state)), "pc_ddim_cfg_step")
+
+
+def pc_ddim_cfg_step_eps(state, eps_cond, eps_uncond, w, layout: PCLayout, abar_t: float, abar_next: float,
+                         eta: float, seed: int, slot: int, project_seams: bool = False, pre_disc=None) -> None:
+    t = _torch()
+    lay = layout.c()
+    n = layout.n_maps * PACKED
+    _check(_lib.load().pc_ddim_cfg_step_eps(
+        _dev(state, t.float32, n, "state"), _dev(eps_cond, t.float32, n, "eps_cond"),
+        _dev(eps_uncond, t.float32, n, "eps_uncond"), _weights(w, layout.n_guidance), ctypes.byref(lay),
+        float(abar_t), float(abar_next), float(eta), seed, slot, int(bool(project_seams)),
+        _dev(pre_disc, t.float32, layout.n_seams * layout.n_guidance * layout.n_traj, "pre_disc"),
+        _stream(state)), "pc_ddim_cfg_step_eps")
 
 
 def pc_ddim_sample(state, x0_cond, x0_uncond, w, layout: PCLayout, n_steps: int, eta: float, seed: int,

@@ -28,10 +28,15 @@ SIGNATURES = {
     "pc_last_error": (ctypes.c_char_p, []),
     "pc_ddim_schedule": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32, ctypes.c_double, ctypes.c_double,
                                           c_double_p, c_double_p]),
+    "pc_ddim_schedule_cosine": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32, ctypes.c_double, ctypes.c_double,
+                                                 c_double_p, c_double_p]),
     "pc_init_state": (ctypes.c_int32, [vp, ctypes.POINTER(Layout), ctypes.c_uint64, vp]),
     "pc_ddim_cfg_step": (ctypes.c_int32, [vp, vp, vp, c_float_p, ctypes.POINTER(Layout), ctypes.c_double,
                                           ctypes.c_double, ctypes.c_double, ctypes.c_uint64, ctypes.c_uint32,
                                           ctypes.c_int32, vp, vp]),
+    "pc_ddim_cfg_step_eps": (ctypes.c_int32, [vp, vp, vp, c_float_p, ctypes.POINTER(Layout), ctypes.c_double,
+                                              ctypes.c_double, ctypes.c_double, ctypes.c_uint64, ctypes.c_uint32,
+                                              ctypes.c_int32, vp, vp]),
     "pc_ddim_sample": (ctypes.c_int32, [vp, vp, vp, c_float_p, ctypes.POINTER(Layout), ctypes.c_int32,
                                         ctypes.c_int32, ctypes.c_double, ctypes.c_double, ctypes.c_double,
                                         ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32, vp]),

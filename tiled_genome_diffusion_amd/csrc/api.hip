@@ -105,6 +105,33 @@ pc_status pc_ddim_schedule(int32_t n_steps, int32_t T, double beta_start, double
     return ok();
 }
 
+pc_status pc_ddim_schedule_cosine(int32_t n_steps, int32_t T, double s, double beta_max, double *abar_t,
+                                  double *abar_next) {
+    if (!abar_t || !abar_next) return fail(PC_ERR_NULL, "output is NULL");
+    if (T < 2) return fail(PC_ERR_PARAM, "T = %d must be >= 2", T);
+    if (n_steps < 1 || T % n_steps != 0) return fail(PC_ERR_PARAM, "n_steps = %d must divide T = %d", n_steps, T);
+    if (!(s >= 0.0 && s < 1.0) || !(beta_max > 0.0 && beta_max < 1.0))
+        return fail(PC_ERR_PARAM, "need 0 <= s < 1 and 0 < beta_max < 1");
+    // f(u) = cos^2(pi/2 (u + s)/(1 + s)); beta_t = min(1 - f((t+1)/T) / f(t/T), beta_max)
+    const double pi = 3.141592653589793;
+    const int stride = T / n_steps;
+    double acc = 1.0;
+    int next_i = n_steps - 1;
+    for (int t = 0; t < T && next_i >= 0; ++t) {
+        const double c0 = cos((static_cast<double>(t) / T + s) / (1.0 + s) * pi / 2.0);
+        const double c1 = cos((static_cast<double>(t + 1) / T + s) / (1.0 + s) * pi / 2.0);
+        double beta = 1.0 - (c1 * c1) / (c0 * c0);
+        if (beta > beta_max) beta = beta_max;
+        acc *= 1.0 - beta;
+        if (t == T - stride * (next_i + 1)) {
+            abar_t[next_i] = acc;
+            --next_i;
+        }
+    }
+    for (int i = 0; i < n_steps; ++i) abar_next[i] = i + 1 < n_steps ? abar_t[i + 1] : 1.0;
+    return ok();
+}
+
 pc_status pc_init_state(float *state, const pc_layout *layout, uint64_t seed, void *stream) {
     return pc_normal_fill(state, layout, seed, 0u, stream);
 }
@@ -131,15 +158,23 @@ pc_status pc_philox_fill(uint32_t *out, const pc_layout *layout, uint64_t seed, 
                       "philox fill launch");
 }
 
-pc_status pc_ddim_cfg_step(float *state, const float *x0_cond, const float *x0_uncond, const float *w,
-                           const pc_layout *layout, double abar_t, double abar_next, double eta, uint64_t seed,
-                           uint32_t slot, int32_t project_seams, float *pre_disc, void *stream) {
-    if (!state || !x0_cond || !x0_uncond || !w) return fail(PC_ERR_NULL, "state, references and w are required");
+}  // extern "C"
+
+namespace {
+
+// Shared by both step entry points: eps_c == nullptr selects the point-mass
+// stand-in on the references, otherwise the per-map noise predictions.
+pc_status ddim_step(const char *name, float *state, const float *x0_cond, const float *x0_uncond, const float *eps_c,
+                    const float *eps_u, const float *w, const pc_layout *layout, double abar_t, double abar_next,
+                    double eta, uint64_t seed, uint32_t slot, int32_t project_seams, float *pre_disc, void *stream) {
     int64_t n = 0;
     pc_status st = check_layout(layout, &n);
     if (st != PC_OK) return st;
-    if (!aligned16(state) || !aligned16(x0_cond) || !aligned16(x0_uncond) || (pre_disc && !aligned16(pre_disc)))
-        return fail(PC_ERR_ALIGN, "device arrays must be 16-byte aligned");
+    const bool eps = eps_c != nullptr;
+    if (eps ? (!aligned16(eps_c) || !aligned16(eps_u)) : (!aligned16(x0_cond) || !aligned16(x0_uncond)))
+        return fail(PC_ERR_ALIGN, "%s: device arrays must be 16-byte aligned", name);
+    if (!aligned16(state) || (pre_disc && !aligned16(pre_disc)))
+        return fail(PC_ERR_ALIGN, "%s: device arrays must be 16-byte aligned", name);
     if (!(abar_t > 0.0 && abar_t < 1.0)) return fail(PC_ERR_PARAM, "abar_t = %g outside (0, 1)", abar_t);
     if (!(abar_next > 0.0 && abar_next <= 1.0)) return fail(PC_ERR_PARAM, "abar_next = %g outside (0, 1]", abar_next);
     if (abar_t > abar_next) return fail(PC_ERR_PARAM, "abar_t %g > abar_next %g", abar_t, abar_next);
@@ -176,10 +211,31 @@ pc_status pc_ddim_cfg_step(float *state, const float *x0_cond, const float *x0_u
     const bool noise = args.c.sigma != 0.0f;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (chains && (project_seams || pre_disc))
-        return hip_status(pc::launch_step_chain(state, x0_cond, x0_uncond, args, chain_args(layout), project_seams != 0,
-                                                pre_disc, noise, s),
+        return hip_status(pc::launch_step_chain(state, x0_cond, x0_uncond, eps_c, eps_u, args, chain_args(layout),
+                                                project_seams != 0, pre_disc, noise, s),
                           "chain step launch");
-    return hip_status(pc::launch_step_indep(state, x0_cond, x0_uncond, args, noise, s), "step launch");
+    return hip_status(pc::launch_step_indep(state, x0_cond, x0_uncond, eps_c, eps_u, args, noise, s), "step launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+pc_status pc_ddim_cfg_step(float *state, const float *x0_cond, const float *x0_uncond, const float *w,
+                           const pc_layout *layout, double abar_t, double abar_next, double eta, uint64_t seed,
+                           uint32_t slot, int32_t project_seams, float *pre_disc, void *stream) {
+    if (!state || !x0_cond || !x0_uncond || !w) return fail(PC_ERR_NULL, "state, references and w are required");
+    return ddim_step("pc_ddim_cfg_step", state, x0_cond, x0_uncond, nullptr, nullptr, w, layout, abar_t, abar_next,
+                     eta, seed, slot, project_seams, pre_disc, stream);
+}
+
+pc_status pc_ddim_cfg_step_eps(float *state, const float *eps_cond, const float *eps_uncond, const float *w,
+                               const pc_layout *layout, double abar_t, double abar_next, double eta, uint64_t seed,
+                               uint32_t slot, int32_t project_seams, float *pre_disc, void *stream) {
+    if (!state || !eps_cond || !eps_uncond || !w)
+        return fail(PC_ERR_NULL, "state, noise predictions and w are required");
+    return ddim_step("pc_ddim_cfg_step_eps", state, nullptr, nullptr, eps_cond, eps_uncond, w, layout, abar_t,
+                     abar_next, eta, seed, slot, project_seams, pre_disc, stream);
 }
 
 pc_status pc_ddim_sample(float *state, const float *x0_cond, const float *x0_uncond, const float *w,

@@ -152,16 +152,24 @@ struct ChainArgs {
     int32_t n_pairs;          // overlap (overlap - 1) / 2
 };
 
-// The fused stand-in denoiser + guidance + DDIM update of one element.  Every
-// rounding is spelled out (explicit fmaf, and the library is built with
-// -ffp-contract=off), so every kernel that steps an element produces the
-// same bits.
-__device__ __forceinline__ float ddim_cfg_element(float x, float x0c, float x0u, float w, const StepCoef &c, float z) {
-    const float eps_c = fmaf(-c.sa, x0c, x) * c.inv_s1a;   // point-mass noise prediction, conditional
-    const float eps_u = fmaf(-c.sa, x0u, x) * c.inv_s1a;   // ... unconditional
+// Guidance combine + DDIM update of one element from its two noise
+// predictions.  Every rounding is spelled out (explicit fmaf, and the library
+// is built with -ffp-contract=off), so every kernel that steps an element
+// produces the same bits.
+__device__ __forceinline__ float ddim_guided_update(float x, float eps_c, float eps_u, float w, const StepCoef &c,
+                                                   float z) {
     const float eps = fmaf(w, eps_c - eps_u, eps_u);       // classifier-free guidance
     const float x0_hat = fmaf(-c.s1a, eps, x) * c.inv_sa;  // predicted clean map
     return fmaf(c.sigma, z, fmaf(c.cdir, eps, c.sap * x0_hat));
+}
+
+// The same with the point-mass stand-in denoiser: the noise predictions are
+// (x - sqrt(a) x0) / sqrt(1 - a) for the conditional and unconditional
+// reference maps.
+__device__ __forceinline__ float ddim_cfg_element(float x, float x0c, float x0u, float w, const StepCoef &c, float z) {
+    const float eps_c = fmaf(-c.sa, x0c, x) * c.inv_s1a;
+    const float eps_u = fmaf(-c.sa, x0u, x) * c.inv_s1a;
+    return ddim_guided_update(x, eps_c, eps_u, w, c, z);
 }
 
 }  // namespace pc

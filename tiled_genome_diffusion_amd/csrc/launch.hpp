@@ -9,11 +9,13 @@ namespace pc {
 hipError_t launch_fill(void *out, int64_t n_maps, uint32_t k0, uint32_t k1, uint32_t slot, bool raw,
                        hipStream_t stream);
 
-hipError_t launch_step_indep(float *state, const float *x0c, const float *x0u, StepArgs a, bool noise,
-                             hipStream_t stream);
+// eps_c == nullptr: point-mass stand-in on the references x0c / x0u;
+// otherwise eps_c / eps_u hold the network's noise predictions per map.
+hipError_t launch_step_indep(float *state, const float *x0c, const float *x0u, const float *eps_c, const float *eps_u,
+                             StepArgs a, bool noise, hipStream_t stream);
 
-hipError_t launch_step_chain(float *state, const float *x0c, const float *x0u, StepArgs a, ChainArgs ch,
-                             bool project, float *pre_disc, bool noise, hipStream_t stream);
+hipError_t launch_step_chain(float *state, const float *x0c, const float *x0u, const float *eps_c, const float *eps_u,
+                             StepArgs a, ChainArgs ch, bool project, float *pre_disc, bool noise, hipStream_t stream);
 
 hipError_t launch_seam_project(float *state, int32_t n_chains, int32_t n_cols, ChainArgs ch, hipStream_t stream);
 

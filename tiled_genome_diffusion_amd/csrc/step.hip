@@ -49,12 +49,23 @@ __device__ __forceinline__ void st_state(float *p, size_t quad, float4 v) {
     __builtin_nontemporal_store(w, reinterpret_cast<f32x4 *>(p) + quad);
 }
 
-__device__ __forceinline__ float4 step4(float4 x, float4 xc, float4 xu, float w, const StepCoef &c, float4 z) {
+// Step four elements.  EPS: (dc, du) are the network's conditional and
+// unconditional noise predictions; otherwise they are the reference maps of
+// the point-mass stand-in.
+template <bool EPS>
+__device__ __forceinline__ float4 step4(float4 x, float4 dc, float4 du, float w, const StepCoef &c, float4 z) {
     float4 y;
-    y.x = ddim_cfg_element(x.x, xc.x, xu.x, w, c, z.x);
-    y.y = ddim_cfg_element(x.y, xc.y, xu.y, w, c, z.y);
-    y.z = ddim_cfg_element(x.z, xc.z, xu.z, w, c, z.z);
-    y.w = ddim_cfg_element(x.w, xc.w, xu.w, w, c, z.w);
+    if (EPS) {
+        y.x = ddim_guided_update(x.x, dc.x, du.x, w, c, z.x);
+        y.y = ddim_guided_update(x.y, dc.y, du.y, w, c, z.y);
+        y.z = ddim_guided_update(x.z, dc.z, du.z, w, c, z.z);
+        y.w = ddim_guided_update(x.w, dc.w, du.w, w, c, z.w);
+    } else {
+        y.x = ddim_cfg_element(x.x, dc.x, du.x, w, c, z.x);
+        y.y = ddim_cfg_element(x.y, dc.y, du.y, w, c, z.y);
+        y.z = ddim_cfg_element(x.z, dc.z, du.z, w, c, z.z);
+        y.w = ddim_cfg_element(x.w, dc.w, du.w, w, c, z.w);
+    }
     return y;
 }
 
@@ -82,23 +93,35 @@ __global__ __launch_bounds__(kThreads) void k_fill(void *__restrict__ out, int64
 
 // ---------------------------------------------------------------------------
 // Independent maps: workgroup -> (region r, weight g, chunk of trajectories).
-// U maps are loaded before any is computed, to keep U loads in flight.
-template <int U, bool NOISE, bool NT>
-__device__ __forceinline__ void step_maps(float *__restrict__ state, size_t map0, uint32_t t0, uint32_t q, float4 xc,
-                                          float4 xu, float w, const StepArgs &a) {
-    float4 x[U];
+// U maps are loaded before any is computed, to keep U loads in flight.  EPS:
+// the noise predictions of each map are read from eps_c / eps_u (same layout
+// as the state) instead of being formed from the region's references.
+template <int U, bool NOISE, bool NT, bool EPS>
+__device__ __forceinline__ void step_maps(float *__restrict__ state, const float *__restrict__ eps_c,
+                                          const float *__restrict__ eps_u, size_t map0, uint32_t t0, uint32_t q,
+                                          float4 xc, float4 xu, float w, const StepArgs &a) {
+    float4 x[U], ec[U], eu[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) x[u] = ld_state<NT>(state, (map0 + u) * kQuads + q);
+    for (int u = 0; u < U; ++u) {
+        x[u] = ld_state<NT>(state, (map0 + u) * kQuads + q);
+        if (EPS) {
+            ec[u] = ld_state<NT>(eps_c, (map0 + u) * kQuads + q);
+            eu[u] = ld_state<NT>(eps_u, (map0 + u) * kQuads + q);
+        }
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const float4 z = NOISE ? philox_normals(q, t0 + u, a.slot, a.k0, a.k1) : make_float4(0.f, 0.f, 0.f, 0.f);
-        st_state<NT>(state, (map0 + u) * kQuads + q, step4(x[u], xc, xu, w, a.c, z));
+        st_state<NT>(state, (map0 + u) * kQuads + q,
+                     EPS ? step4<true>(x[u], ec[u], eu[u], w, a.c, z) : step4<false>(x[u], xc, xu, w, a.c, z));
     }
 }
 
-template <int U, bool NOISE, bool NT>
+template <int U, bool NOISE, bool NT, bool EPS>
 __global__ __launch_bounds__(kThreads) void k_step_indep(float *__restrict__ state, const float *__restrict__ x0c,
-                                                         const float *__restrict__ x0u, StepArgs a) {
+                                                         const float *__restrict__ x0u,
+                                                         const float *__restrict__ eps_c,
+                                                         const float *__restrict__ eps_u, StepArgs a) {
     const uint32_t q = threadIdx.x;
     if (q >= kQuads) return;
     const uint32_t b = xcd_remap(blockIdx.x, gridDim.x);
@@ -107,14 +130,18 @@ __global__ __launch_bounds__(kThreads) void k_step_indep(float *__restrict__ sta
     const int r = rg / a.G;
     const int g = rg - r * a.G;
     const float w = a.w[g];
-    const float4 xc = ld4(x0c, static_cast<size_t>(r) * kQuads + q);
-    const float4 xu = ld4(x0u, static_cast<size_t>(r) * kQuads + q);
+    float4 xc = make_float4(0.f, 0.f, 0.f, 0.f), xu = xc;
+    if (!EPS) {
+        xc = ld4(x0c, static_cast<size_t>(r) * kQuads + q);
+        xu = ld4(x0u, static_cast<size_t>(r) * kQuads + q);
+    }
     const int s0 = chunk * a.maps_per_block;
     const int s1 = s0 + a.maps_per_block < a.S ? s0 + a.maps_per_block : a.S;
     const uint32_t t_base = static_cast<uint32_t>(rg) * static_cast<uint32_t>(a.S);
     int s = s0;
-    for (; s + U <= s1; s += U) step_maps<U, NOISE, NT>(state, t_base + s, t_base + s, q, xc, xu, w, a);
-    for (; s < s1; ++s) step_maps<1, NOISE, NT>(state, t_base + s, t_base + s, q, xc, xu, w, a);
+    for (; s + U <= s1; s += U)
+        step_maps<U, NOISE, NT, EPS>(state, eps_c, eps_u, t_base + s, t_base + s, q, xc, xu, w, a);
+    for (; s < s1; ++s) step_maps<1, NOISE, NT, EPS>(state, eps_c, eps_u, t_base + s, t_base + s, q, xc, xu, w, a);
 }
 
 // ---------------------------------------------------------------------------
@@ -138,9 +165,11 @@ __global__ __launch_bounds__(kThreads) void k_step_indep(float *__restrict__ sta
 // otherwise idle lane per map sums the squared seam differences in pair order
 // and stores the RMS per (seam, g, s).  LDS is double-buffered by iteration
 // parity, so one barrier per iteration suffices.
-template <int U, bool PROJECT, bool DISC, bool NOISE, bool NT>
+template <int U, bool PROJECT, bool DISC, bool NOISE, bool NT, bool EPS>
 __global__ __launch_bounds__(kThreads) void k_step_chain(float *__restrict__ state, const float *__restrict__ x0c,
-                                                         const float *__restrict__ x0u, StepArgs a, ChainArgs ch,
+                                                         const float *__restrict__ x0u,
+                                                         const float *__restrict__ eps_c,
+                                                         const float *__restrict__ eps_u, StepArgs a, ChainArgs ch,
                                                          float *__restrict__ pre_disc) {
     static_assert(U <= kThreads - kQuads, "the discrepancy of map u is summed by idle lane kQuads + u");
     __shared__ float s_right[2][U][kMaxPairs];  // tile k's stepped right-seam values
@@ -191,12 +220,12 @@ __global__ __launch_bounds__(kThreads) void k_step_chain(float *__restrict__ sta
     const bool t1 = own && halo;  // tile 0 only
 
     float4 rc0 = make_float4(0.f, 0.f, 0.f, 0.f), ru0 = rc0, rc1 = rc0, ru1 = rc0;
-    if (t0) {
+    if (t0 && !EPS) {
         const size_t rr = static_cast<size_t>(r + (t0_halo ? 1 : 0));
         rc0 = ld4(x0c, rr * kQuads + q);
         ru0 = ld4(x0u, rr * kQuads + q);
     }
-    if (t1) {
+    if (t1 && !EPS) {
         rc1 = ld4(x0c, static_cast<size_t>(r + 1) * kQuads + q);
         ru1 = ld4(x0u, static_cast<size_t>(r + 1) * kQuads + q);
     }
@@ -210,12 +239,26 @@ __global__ __launch_bounds__(kThreads) void k_step_chain(float *__restrict__ sta
         const int nu = s1 - sb < U ? s1 - sb : U;
         float4 y0[U], y1[U];
         {
-            float4 x0[U], x1[U];
+            float4 x0[U], x1[U], e0c[U], e0u[U], e1c[U], e1u[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 if (u < nu) {
-                    if (t0) x0[u] = ld_state<NT>(state, (t_base + sb + u + off0) * kQuads + q);
-                    if (t1) x1[u] = ld_state<NT>(state, (t_base + sb + u + n_cols) * kQuads + q);
+                    const size_t m0 = (t_base + sb + u + off0) * kQuads + q;
+                    const size_t m1 = (t_base + sb + u + n_cols) * kQuads + q;
+                    if (t0) {
+                        x0[u] = ld_state<NT>(state, m0);
+                        if (EPS) {
+                            e0c[u] = ld_state<NT>(eps_c, m0);
+                            e0u[u] = ld_state<NT>(eps_u, m0);
+                        }
+                    }
+                    if (t1) {
+                        x1[u] = ld_state<NT>(state, m1);
+                        if (EPS) {
+                            e1c[u] = ld_state<NT>(eps_c, m1);
+                            e1u[u] = ld_state<NT>(eps_u, m1);
+                        }
+                    }
                 }
             }
 #pragma unroll
@@ -226,13 +269,15 @@ __global__ __launch_bounds__(kThreads) void k_step_chain(float *__restrict__ sta
                     const uint32_t m0 = static_cast<uint32_t>(map + off0);
                     const float4 z = NOISE ? philox_normals(q, m0, a.slot, a.k0, a.k1)
                                            : make_float4(0.f, 0.f, 0.f, 0.f);
-                    y0[u] = step4(x0[u], rc0, ru0, w, a.c, z);
+                    y0[u] = EPS ? step4<true>(x0[u], e0c[u], e0u[u], w, a.c, z)
+                                : step4<false>(x0[u], rc0, ru0, w, a.c, z);
                 }
                 if (t1) {
                     const uint32_t m1 = static_cast<uint32_t>(map + n_cols);
                     const float4 z = NOISE ? philox_normals(q, m1, a.slot, a.k0, a.k1)
                                            : make_float4(0.f, 0.f, 0.f, 0.f);
-                    y1[u] = step4(x1[u], rc1, ru1, w, a.c, z);
+                    y1[u] = EPS ? step4<true>(x1[u], e1c[u], e1u[u], w, a.c, z)
+                                : step4<false>(x1[u], rc1, ru1, w, a.c, z);
                 }
                 // right-seam values of tile k (task 0 of own lanes)
                 if (own && owns_seam && right_quad) {
@@ -306,27 +351,31 @@ hipError_t launch_fill(void *out, int64_t n_maps, uint32_t k0, uint32_t k1, uint
     return hipGetLastError();
 }
 
-hipError_t launch_step_indep(float *state, const float *x0c, const float *x0u, StepArgs a, bool noise,
-                             hipStream_t stream) {
+hipError_t launch_step_indep(float *state, const float *x0c, const float *x0u, const float *eps_c, const float *eps_u,
+                             StepArgs a, bool noise, hipStream_t stream) {
     a.maps_per_block = kIndepMaps;
     a.blocks_per_rg = (a.S + a.maps_per_block - 1) / a.maps_per_block;
     const int64_t n_maps = static_cast<int64_t>(a.R) * a.G * a.S;
     const int64_t blocks = static_cast<int64_t>(a.R) * a.G * a.blocks_per_rg;
     const dim3 grid(static_cast<uint32_t>(blocks));
     const bool nt = static_cast<size_t>(n_maps) * kPacked * 4 > kStreamBytes;
-#define PC_INDEP(N, T) \
-    hipLaunchKernelGGL((k_step_indep<kIndepU, N, T>), grid, dim3(kThreads), 0, stream, state, x0c, x0u, a)
+    const bool eps = eps_c != nullptr;
+#define PC_INDEP(N, T, E) \
+    hipLaunchKernelGGL((k_step_indep<kIndepU, N, T, E>), grid, dim3(kThreads), 0, stream, state, x0c, x0u, eps_c, eps_u, a)
+#define PC_INDEP_E(N, T) \
+    if (eps) PC_INDEP(N, T, true); else PC_INDEP(N, T, false)
     if (noise) {
-        if (nt) PC_INDEP(true, true); else PC_INDEP(true, false);
+        if (nt) PC_INDEP_E(true, true); else PC_INDEP_E(true, false);
     } else {
-        if (nt) PC_INDEP(false, true); else PC_INDEP(false, false);
+        if (nt) PC_INDEP_E(false, true); else PC_INDEP_E(false, false);
     }
+#undef PC_INDEP_E
 #undef PC_INDEP
     return hipGetLastError();
 }
 
-hipError_t launch_step_chain(float *state, const float *x0c, const float *x0u, StepArgs a, ChainArgs ch,
-                             bool project, float *pre_disc, bool noise, hipStream_t stream) {
+hipError_t launch_step_chain(float *state, const float *x0c, const float *x0u, const float *eps_c, const float *eps_u,
+                             StepArgs a, ChainArgs ch, bool project, float *pre_disc, bool noise, hipStream_t stream) {
     const int64_t n_maps = static_cast<int64_t>(a.R) * a.G * a.S;
     int64_t mpb = (n_maps / kChainGrid) & ~int64_t(1);
     mpb = mpb < kChainMapsMin ? kChainMapsMin : (mpb > kChainMapsMax ? kChainMapsMax : mpb);
@@ -336,11 +385,14 @@ hipError_t launch_step_chain(float *state, const float *x0c, const float *x0u, S
     const dim3 grid(static_cast<uint32_t>(blocks));
     const bool disc = pre_disc != nullptr;
     const bool nt = static_cast<size_t>(n_maps) * kPacked * 4 > kStreamBytes;
-#define PC_CHAIN(P, D, N, T)                                                                                     \
-    hipLaunchKernelGGL((k_step_chain<kChainU, P, D, N, T>), grid, dim3(kThreads), 0, stream, state, x0c, x0u, a, \
-                       ch, pre_disc)
+    const bool eps = eps_c != nullptr;
+#define PC_CHAIN(P, D, N, T, E)                                                                                 \
+    hipLaunchKernelGGL((k_step_chain<kChainU, P, D, N, T, E>), grid, dim3(kThreads), 0, stream, state, x0c, x0u, \
+                       eps_c, eps_u, a, ch, pre_disc)
+#define PC_CHAIN_E(P, D, N, T) \
+    if (eps) PC_CHAIN(P, D, N, T, true); else PC_CHAIN(P, D, N, T, false)
 #define PC_CHAIN_NT(P, D, N) \
-    if (nt) PC_CHAIN(P, D, N, true); else PC_CHAIN(P, D, N, false)
+    if (nt) PC_CHAIN_E(P, D, N, true); else PC_CHAIN_E(P, D, N, false)
     if (project) {
         if (disc) {
             if (noise) PC_CHAIN_NT(true, true, true); else PC_CHAIN_NT(true, true, false);
@@ -351,6 +403,7 @@ hipError_t launch_step_chain(float *state, const float *x0c, const float *x0u, S
         if (noise) PC_CHAIN_NT(false, true, true); else PC_CHAIN_NT(false, true, false);
     }
 #undef PC_CHAIN_NT
+#undef PC_CHAIN_E
 #undef PC_CHAIN
     return hipGetLastError();
 }
