@@ -203,6 +203,17 @@ PC_API pc_status pc_seam_discrepancy(const float *state, const pc_layout *layout
                               void *stream);
 
 /*
+ * Seam discrepancy in the paper's form (section 5.5, Eq. (6); the equation
+ * itself was lost, read from its description): per seam and guidance weight,
+ * the mean over the shared pairs of |mean_s left copy - mean_s right copy|,
+ * the sample means taken over the S trajectories.  Sums run in float64 in
+ * trajectory order; deterministic.
+ *   out  device float [n_chains*(chain_len-1)][G], written.
+ * Errors: NULL pointers; bad layout; chain_len < 2.
+ */
+PC_API pc_status pc_seam_mean_abs(const float *state, const pc_layout *layout, float *out, void *stream);
+
+/*
  * Classical (Torgerson) MDS per map, the distance-geometry initialiser that
  * turns a final map into a 64-bead point cloud (sections 3.1 and 5.5):
  * B = -1/2 J (D o D) J, its three largest eigenpairs by block subspace
@@ -220,6 +231,25 @@ PC_API pc_status pc_seam_discrepancy(const float *state, const pc_layout *layout
  */
 PC_API pc_status pc_mds_recover(const float *maps, int64_t n_maps, float *coords, float *eigvals,
                          int32_t max_iters, void *stream);
+
+/*
+ * Chain stitching (section 5.5 and Figure 4: each tile's point cloud, rigidly
+ * aligned on the shared beads, gives a chromosome-scale chain; the residual
+ * after alignment is the coordinate-level seam diagnostic).  For every chain
+ * and (g, s), tile 0 keeps its frame and tile k+1 is moved onto the aligned
+ * tile k by the orthogonal map and translation that best superpose its first
+ * `overlap` beads on tile k's last `overlap` beads (orthogonal Procrustes;
+ * reflections allowed, since a distance map fixes a point cloud only up to
+ * O(3)).  A shared bead takes the mean of its two aligned positions.
+ *   coords    device float [R][G][S][64][3] (pc_mds_recover's output).
+ *   chain     device float [n_chains][G][S][(chain_len-1)(64-overlap)+64][3], written.
+ *   residual  device float [n_chains*(chain_len-1)][G][S], written: RMS
+ *             distance over the shared beads after aligning seam k.
+ * Shared beads must not be coplanar (the alignment is then not unique).
+ * Errors: NULL pointers; bad layout; chain_len < 2.
+ */
+PC_API pc_status pc_kabsch_stitch(const float *coords, const pc_layout *layout, float *chain, float *residual,
+                                  void *stream);
 
 /* Diagnostics ----------------------------------------------------------- */
 

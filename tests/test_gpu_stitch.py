@@ -1,0 +1,96 @@
+"""GPU parity of chain stitching and of the paper-form seam discrepancy."""
+
+import numpy as np
+import pytest
+
+import tiled_genome_diffusion_amd as pc
+from gpu_util import layout_of, map_index, run_steps, say, torch_dev, upload_refs
+from oracle import seam, stitch
+from workloads import Workload, get, random_walk, walk_rng
+
+pytestmark = pytest.mark.gpu
+
+
+def _orth(rng, reflect):
+    q, r = np.linalg.qr(rng.standard_normal((3, 3)))
+    q = q * np.sign(np.diag(r))
+    if reflect:
+        q[:, 0] *= -1
+    return q
+
+
+def test_stitch_synthetic_rigid_motions():
+    torch, dev = torch_dev()
+    rng = np.random.default_rng(0)
+    L, O, n_chains, S = 6, 12, 3, 4
+    lay = pc.PCLayout(n_chains * L, 1, S, L, O)
+    say("stitch: per-tile random rigid motions and reflections")
+    coords = np.zeros((n_chains * L, 1, S, 64, 3), dtype=np.float32)
+    truth = {}
+    for c in range(n_chains):
+        for s in range(S):
+            walk = random_walk((L - 1) * 52 + 64, walk_rng(c, s, 77), None)
+            truth[c, s] = walk
+            for k in range(L):
+                t = walk[k * 52:k * 52 + 64]
+                coords[c * L + k, 0, s] = t @ _orth(rng, (k + s) % 2 == 1) + rng.standard_normal(3) * 5
+    cd = torch.from_numpy(coords.reshape(-1)).to(dev)
+    nb = (L - 1) * 52 + 64
+    chain = torch.empty(n_chains * S * nb * 3, dtype=torch.float32, device=dev)
+    resid = torch.empty(n_chains * (L - 1) * S, dtype=torch.float32, device=dev)
+    pc.pc_kabsch_stitch(cd, lay, chain, resid)
+    got = chain.cpu().numpy().reshape(n_chains, S, nb, 3)
+    res = resid.cpu().numpy().reshape(n_chains, L - 1, S)
+    for c in range(n_chains):
+        for s in range(S):
+            want, wres = stitch.stitch_chain(coords[c * L:(c + 1) * L, 0, s].astype(np.float64), O)
+            ext = np.abs(want).max()
+            assert np.abs(got[c, s] - want).max() <= 1e-4 * ext
+            # tiles were rounded to float32 after their motions: residuals sit at float32 rounding
+            assert np.all(res[c, :, s] <= 1e-4 * ext) and np.all(wres <= 1e-5 * ext)
+
+
+def test_stitch_end_to_end_chr22():
+    torch, dev = torch_dev()
+    wl = get("chr22_chain")
+    lay = layout_of(wl)
+    say("stitch: chr22 chain sampled, MDS, stitched")
+    refs = upload_refs(wl, 0)
+    _, state, _ = run_steps(wl, 0, 50, [0], set(), refs=refs)
+    coords = torch.empty(lay.n_maps * 192, dtype=torch.float32, device=dev)
+    pc.pc_mds_recover(state, coords)
+    nb = wl.chain_beads
+    chain = torch.empty(wl.n_guidance * wl.n_traj * nb * 3, dtype=torch.float32, device=dev)
+    resid = torch.empty(lay.n_seams * wl.n_guidance * wl.n_traj, dtype=torch.float32, device=dev)
+    pc.pc_kabsch_stitch(coords, lay, chain, resid)
+    xyz = coords.cpu().numpy().reshape(lay.n_maps, 64, 3)
+    got = chain.cpu().numpy().reshape(wl.n_guidance, wl.n_traj, nb, 3)
+    res = resid.cpu().numpy().reshape(wl.chain_len - 1, wl.n_guidance, wl.n_traj)
+    for g, s in [(0, 0), (1, 5), (0, 255)]:
+        rows = [map_index(wl, k, g, s) for k in range(wl.chain_len)]
+        want, wres = stitch.stitch_chain(xyz[rows].astype(np.float64), wl.overlap)
+        ext = np.abs(want).max()
+        assert np.abs(got[g, s] - want).max() <= 1e-4 * ext
+        assert np.allclose(res[:, g, s], wres, atol=1e-4 * ext, rtol=1e-3)
+        # the final maps are the reference windows of one chain walk: the seams close up
+        assert wres.max() <= 1e-3
+
+
+def test_seam_mean_abs_matches_oracle():
+    torch, dev = torch_dev()
+    wl = get("chr22_chain")
+    lay = layout_of(wl)
+    say("paper-form seam discrepancy on an unprojected and a projected chain state")
+    refs = upload_refs(wl, 1)
+    _, state, _ = run_steps(wl, 1, 50, [0], set(), project=False, refs=refs, stop_after=10)
+    out = torch.empty(lay.n_seams * wl.n_guidance, dtype=torch.float32, device=dev)
+    pc.pc_seam_mean_abs(state, lay, out)
+    got = out.cpu().numpy().reshape(wl.chain_len - 1, wl.n_guidance)
+    x = state.view(wl.chain_len, wl.n_guidance, wl.n_traj, 2016).cpu().numpy().astype(np.float64)
+    for g in range(wl.n_guidance):
+        want = seam.discrepancy_mean_abs(x[:, g], wl.overlap)
+        assert np.allclose(got[:, g], want, rtol=1e-5, atol=1e-6)
+        assert np.all(want > 0)
+    pc.pc_seam_project(state, lay)
+    pc.pc_seam_mean_abs(state, lay, out)
+    assert torch.count_nonzero(out).item() == 0

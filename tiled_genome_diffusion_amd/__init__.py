@@ -17,7 +17,7 @@ from . import _lib
 
 __all__ = ["PCError", "PCLayout", "PACKED", "BEADS", "pc_version", "pc_last_error", "pc_ddim_schedule",
            "pc_ddim_schedule_cosine", "pc_init_state", "pc_ddim_cfg_step", "pc_ddim_cfg_step_eps", "pc_ddim_sample", "pc_seam_project", "pc_seam_discrepancy",
-           "pc_mds_recover", "pc_philox_block", "pc_philox_fill", "pc_normal_fill", "pc_seam_index_map"]
+           "pc_seam_mean_abs", "pc_mds_recover", "pc_kabsch_stitch", "pc_philox_block", "pc_philox_fill", "pc_normal_fill", "pc_seam_index_map"]
 
 BEADS = 64
 PACKED = 2016
@@ -179,6 +179,14 @@ def pc_seam_discrepancy(state, layout: PCLayout, rms, summary=None) -> None:
         _dev(summary, t.float32, 2, "summary"), _stream(state)), "pc_seam_discrepancy")
 
 
+def pc_seam_mean_abs(state, layout: PCLayout, out) -> None:
+    t = _torch()
+    lay = layout.c()
+    _check(_lib.load().pc_seam_mean_abs(
+        _dev(state, t.float32, layout.n_maps * PACKED, "state"), ctypes.byref(lay),
+        _dev(out, t.float32, layout.n_seams * layout.n_guidance, "out"), _stream(state)), "pc_seam_mean_abs")
+
+
 def pc_mds_recover(maps, coords, eigvals=None, max_iters: int = 0) -> None:
     t = _torch()
     n = maps.numel() // PACKED
@@ -188,6 +196,18 @@ def pc_mds_recover(maps, coords, eigvals=None, max_iters: int = 0) -> None:
                                       _dev(coords, t.float32, n * BEADS * 3, "coords"),
                                       _dev(eigvals, t.float32, n * 3, "eigvals"), max_iters, _stream(maps)),
            "pc_mds_recover")
+
+
+def pc_kabsch_stitch(coords, layout: PCLayout, chain, residual) -> None:
+    t = _torch()
+    lay = layout.c()
+    n_chains = layout.n_regions // layout.chain_len
+    n_beads = (layout.chain_len - 1) * (BEADS - layout.overlap) + BEADS
+    _check(_lib.load().pc_kabsch_stitch(
+        _dev(coords, t.float32, layout.n_maps * BEADS * 3, "coords"), ctypes.byref(lay),
+        _dev(chain, t.float32, n_chains * layout.n_guidance * layout.n_traj * n_beads * 3, "chain"),
+        _dev(residual, t.float32, layout.n_seams * layout.n_guidance * layout.n_traj, "residual"),
+        _stream(coords)), "pc_kabsch_stitch")
 
 
 def pc_philox_block(ctr, seed: int):

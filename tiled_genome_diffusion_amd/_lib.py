@@ -42,7 +42,9 @@ SIGNATURES = {
                                         ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32, vp]),
     "pc_seam_project": (ctypes.c_int32, [vp, ctypes.POINTER(Layout), vp]),
     "pc_seam_discrepancy": (ctypes.c_int32, [vp, ctypes.POINTER(Layout), vp, vp, vp]),
+    "pc_seam_mean_abs": (ctypes.c_int32, [vp, ctypes.POINTER(Layout), vp, vp]),
     "pc_mds_recover": (ctypes.c_int32, [vp, ctypes.c_int64, vp, vp, ctypes.c_int32, vp]),
+    "pc_kabsch_stitch": (ctypes.c_int32, [vp, ctypes.POINTER(Layout), vp, vp, vp]),
     "pc_philox_block": (ctypes.c_int32, [c_u32_p, c_u32_p, ctypes.c_uint64]),
     "pc_philox_fill": (ctypes.c_int32, [vp, ctypes.POINTER(Layout), ctypes.c_uint64, ctypes.c_uint32, vp]),
     "pc_normal_fill": (ctypes.c_int32, [vp, ctypes.POINTER(Layout), ctypes.c_uint64, ctypes.c_uint32, vp]),

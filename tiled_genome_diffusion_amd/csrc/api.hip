@@ -301,6 +301,19 @@ pc_status pc_seam_discrepancy(const float *state, const pc_layout *layout, float
                       "seam discrepancy launch");
 }
 
+pc_status pc_seam_mean_abs(const float *state, const pc_layout *layout, float *out, void *stream) {
+    if (!state || !out) return fail(PC_ERR_NULL, "state and out are required");
+    int64_t n = 0;
+    const pc_status st = check_layout(layout, &n);
+    if (st != PC_OK) return st;
+    if (layout->chain_len < 2) return fail(PC_ERR_SHAPE, "seam discrepancy needs chain_len >= 2");
+    if (!aligned16(state)) return fail(PC_ERR_ALIGN, "state not 16-byte aligned");
+    return hip_status(pc::launch_seam_mean_abs(state, layout->n_regions / layout->chain_len, layout->n_guidance,
+                                               layout->n_traj, chain_args(layout), out,
+                                               static_cast<hipStream_t>(stream)),
+                      "seam mean-abs launch");
+}
+
 pc_status pc_mds_recover(const float *maps, int64_t n_maps, float *coords, float *eigvals, int32_t max_iters,
                          void *stream) {
     if (!maps || !coords) return fail(PC_ERR_NULL, "maps and coords are required");
@@ -312,6 +325,21 @@ pc_status pc_mds_recover(const float *maps, int64_t n_maps, float *coords, float
         return fail(PC_ERR_ALIGN, "device arrays must be 16-byte aligned");
     return hip_status(pc::launch_mds(maps, n_maps, coords, eigvals, max_iters, static_cast<hipStream_t>(stream)),
                       "mds launch");
+}
+
+pc_status pc_kabsch_stitch(const float *coords, const pc_layout *layout, float *chain, float *residual,
+                           void *stream) {
+    if (!coords || !chain || !residual) return fail(PC_ERR_NULL, "coords, chain and residual are required");
+    int64_t n = 0;
+    const pc_status st = check_layout(layout, &n);
+    if (st != PC_OK) return st;
+    if (layout->chain_len < 2) return fail(PC_ERR_SHAPE, "stitching needs chain_len >= 2");
+    if (!aligned16(coords) || !aligned16(chain) || !aligned16(residual))
+        return fail(PC_ERR_ALIGN, "device arrays must be 16-byte aligned");
+    return hip_status(pc::launch_stitch(coords, layout->n_regions / layout->chain_len, layout->n_guidance,
+                                        layout->n_traj, chain_args(layout), chain, residual,
+                                        static_cast<hipStream_t>(stream)),
+                      "stitch launch");
 }
 
 pc_status pc_philox_block(uint32_t out[4], const uint32_t ctr[4], uint64_t seed) {

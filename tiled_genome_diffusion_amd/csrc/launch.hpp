@@ -22,6 +22,12 @@ hipError_t launch_seam_project(float *state, int32_t n_chains, int32_t n_cols, C
 hipError_t launch_seam_discrepancy(const float *state, int32_t n_chains, int32_t n_cols, ChainArgs ch, float *rms,
                                    float *summary, hipStream_t stream);
 
+hipError_t launch_seam_mean_abs(const float *state, int32_t n_chains, int32_t G, int32_t S, ChainArgs ch, float *out,
+                                hipStream_t stream);
+
+hipError_t launch_stitch(const float *coords, int32_t n_chains, int32_t G, int32_t S, ChainArgs ch, float *chain,
+                         float *resid, hipStream_t stream);
+
 hipError_t launch_mds(const float *maps, int64_t n_maps, float *coords, float *eigvals, int32_t max_iters,
                       hipStream_t stream);
 

@@ -28,26 +28,6 @@ namespace {
 constexpr int kLanes = 64;
 constexpr int kBlk = 4;
 
-// Wavefront sum by DPP: quad permutes, then the half-row and row mirrors
-// leave every lane of a 16-lane row holding the row total (each step adds a
-// value to its mirror image, so the lanes of a row round identically); row
-// broadcasts 15 and 31 fold the four rows into lane 63, which is read back
-// as a wave-uniform value.  Six full-rate DPP adds and one readlane, in a
-// fixed order.
-template <int CTRL, int ROW_MASK = 0xF>
-__device__ __forceinline__ float dpp(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
-}
-__device__ __forceinline__ float wave_sum(float v) {
-    v += dpp<0xB1>(v);         // quad_perm [1,0,3,2]
-    v += dpp<0x4E>(v);         // quad_perm [2,3,0,1]
-    v += dpp<0x141>(v);        // row_half_mirror
-    v += dpp<0x140>(v);        // row_mirror
-    v += dpp<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
-    v += dpp<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-}
-
 // Fixed pseudo-random start vectors (an integer hash of (bead, column)).
 __device__ __forceinline__ float start_vec(int i, int k) {
     uint32_t x = static_cast<uint32_t>(i) * 0x9E3779B1u + static_cast<uint32_t>(k) * 0x85EBCA77u + 0x165667B1u;

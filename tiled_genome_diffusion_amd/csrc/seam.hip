@@ -58,6 +58,41 @@ __global__ __launch_bounds__(256) void k_seam_disc(const float *__restrict__ sta
     rms[sc] = sqrtf(acc / static_cast<float>(NP));
 }
 
+// Paper-form seam discrepancy: one workgroup per (chain, seam, weight g);
+// lane p < NP sums pair p's left and right copies over the S trajectories in
+// index order (float64), and the mean over pairs of |mean left - mean right|
+// is a fixed-order tree over the lanes.
+__global__ __launch_bounds__(512) void k_seam_mean_abs(const float *__restrict__ state, int32_t G, int32_t S,
+                                                       ChainArgs ch, float *__restrict__ out) {
+    __shared__ double s_acc[512];
+    const int NP = ch.n_pairs, L = ch.chain_len;
+    const int cj = static_cast<int>(blockIdx.x) / G;   // c (L - 1) + j
+    const int g = static_cast<int>(blockIdx.x) - cj * G;
+    const int c = cj / (L - 1);
+    const int j = cj - c * (L - 1);
+    const int n_cols = G * S;
+    double v = 0.0;
+    for (int p = threadIdx.x; p < NP; p += 512) {
+        int li, ri;
+        pair_indices(p, ch.overlap, li, ri);
+        const float *xl = state + (static_cast<size_t>(c * L + j) * n_cols + static_cast<size_t>(g) * S) * kPacked + li;
+        const float *xr = xl + static_cast<size_t>(n_cols) * kPacked - li + ri;
+        double sl = 0.0, sr = 0.0;
+        for (int s = 0; s < S; ++s) {
+            sl += xl[static_cast<size_t>(s) * kPacked];
+            sr += xr[static_cast<size_t>(s) * kPacked];
+        }
+        v += fabs(sl - sr) / S;
+    }
+    s_acc[threadIdx.x] = v;
+    __syncthreads();
+    for (int h = 256; h > 0; h >>= 1) {
+        if (static_cast<int>(threadIdx.x) < h) s_acc[threadIdx.x] += s_acc[threadIdx.x + h];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) out[blockIdx.x] = static_cast<float>(s_acc[0] / NP);
+}
+
 // Mean and max of n values by one workgroup: each lane folds a strided slice
 // in index order, then a fixed tree over the lanes.  Deterministic.
 __global__ __launch_bounds__(256) void k_mean_max(const float *__restrict__ v, int64_t n, float *__restrict__ out) {
@@ -93,6 +128,15 @@ hipError_t launch_seam_project(float *state, int32_t n_chains, int32_t n_cols, C
     const int64_t blocks = (total + 255) / 256;
     hipLaunchKernelGGL(k_seam_project, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream, state, total,
                        n_cols, ch);
+    return hipGetLastError();
+}
+
+hipError_t launch_seam_mean_abs(const float *state, int32_t n_chains, int32_t G, int32_t S, ChainArgs ch, float *out,
+                                hipStream_t stream) {
+    const int64_t blocks = static_cast<int64_t>(n_chains) * (ch.chain_len - 1) * G;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_seam_mean_abs, dim3(static_cast<uint32_t>(blocks)), dim3(512), 0, stream, state, G, S, ch,
+                       out);
     return hipGetLastError();
 }
 
