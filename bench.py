@@ -44,6 +44,9 @@ def parse():
     p.add_argument("--eps-buffers", action="store_true",
                    help="step with noise predictions read from buffers (the interface of a trained denoiser) "
                         "instead of the point-mass stand-in: 16 B per element-step instead of 8")
+    p.add_argument("--sync-ablation", default="",
+                   help="comma-separated projection intervals K (0 = never) for a sync-frequency ablation on a "
+                        "chain workload; prints one JSON line with a row per K")
     p.add_argument("--copy-only", action="store_true",
                    help="time a plain device-to-device copy of the workload's state size instead "
                         "(the calibration kernel for the HBM byte counters)")
@@ -85,6 +88,85 @@ def copy_only(args, wl):
     dt = (time.perf_counter() - t0) / args.steps
     print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "ms": dt * 1e3,
                       "gbs": 2 * n * 4 / dt / 1e9, "workload": wl.name}), flush=True)
+
+
+def sync_ablation(args, wl, n_steps):
+    """Projection every K steps (ParaChromo's synchronisation interval, section 5.7): wall time of
+    the step loop relative to no projection, the paper-form seam discrepancy after the last step and
+    averaged over all steps, and the drift of non-overlap entries from the unsynchronised run."""
+    import numpy as np
+    import torch
+
+    import tiled_genome_diffusion_amd as pc
+    from workloads import reference_maps
+
+    if wl.chain_len < 2:
+        raise SystemExit("--sync-ablation needs a chain workload")
+    dev = torch.device("cuda:0")
+    lay = pc.PCLayout(wl.n_regions, wl.n_guidance, wl.n_traj, wl.chain_len, wl.overlap)
+    x0c, x0u = reference_maps(wl, args.seed)
+    x0c_d, x0u_d = torch.from_numpy(x0c).to(dev), torch.from_numpy(x0u).to(dev)
+    state = torch.empty(lay.n_maps * pc.PACKED, dtype=torch.float32, device=dev)
+    disc = torch.empty(lay.n_seams * lay.n_guidance, dtype=torch.float32, device=dev)
+    a_t, a_n = pc.pc_ddim_schedule(n_steps)
+    li, ri = [], []
+    for p_, q_ in [(p_, q_) for p_ in range(wl.overlap) for q_ in range(p_ + 1, wl.overlap)]:
+        off = 64 - wl.overlap
+        li.append((off + p_) * (127 - (off + p_)) // 2 + (off + q_ - (off + p_) - 1))
+        ri.append(p_ * (127 - p_) // 2 + (q_ - p_ - 1))
+    keep = np.ones((wl.chain_len, pc.PACKED), dtype=bool)
+    keep[:-1, li] = False
+    keep[1:, ri] = False
+    tile = (np.arange(lay.n_maps) // (wl.n_guidance * wl.n_traj)) % wl.chain_len
+    keep_d = torch.as_tensor(keep[tile], device=dev)
+    mid = n_steps // 2
+
+    def run(K, measure):
+        pc.pc_init_state(state, lay, args.seed)
+        traj, mid_state = [], None
+        for i in range(n_steps):
+            proj = K > 0 and (i + 1) % K == 0
+            pc.pc_ddim_cfg_step(state, x0c_d, x0u_d, list(wl.w), lay, a_t[i], a_n[i], wl.eta, args.seed, i + 1,
+                                project_seams=proj)
+            if measure:
+                pc.pc_seam_mean_abs(state, lay, disc)
+                traj.append(float(disc.mean()))
+                if i + 1 == mid:
+                    mid_state = state.view(lay.n_maps, pc.PACKED)[keep_d].clone()
+        return traj, mid_state
+
+    def timed(K):
+        # the whole chain from the C side (one launch per step, no host work in between)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        pc.pc_ddim_sample(state, x0c_d, x0u_d, list(wl.w), lay, n_steps, wl.eta, args.seed, project_every=K)
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(args.steps):
+            pc.pc_init_state(state, lay, args.seed)
+            ev[0].record()
+            pc.pc_ddim_sample(state, x0c_d, x0u_d, list(wl.w), lay, n_steps, wl.eta, args.seed, project_every=K,
+                              init=False)
+            ev[1].record()
+            torch.cuda.synchronize()
+            ms.append(ev[0].elapsed_time(ev[1]))
+        return float(np.median(ms)) * 1e-3
+
+    ks = [int(k) for k in args.sync_ablation.split(",")]
+    base_traj, base_mid = run(0, True)
+    base_t = timed(0)
+    rows = []
+    for K in ks:
+        traj, mid_state = run(K, True)
+        drift = float(torch.linalg.vector_norm(mid_state - base_mid) / torch.linalg.vector_norm(base_mid))
+        t = timed(K)
+        rows.append({"K": K, "step_loop_ms": t * 1e3, "wall_ratio": t / base_t,
+                     "final_mean_abs_disc": traj[-1], "mean_abs_disc_over_steps": float(np.mean(traj)),
+                     "nonoverlap_drift_at_step_%d" % mid: drift})
+    print(json.dumps({"metric": "sync-interval ablation", "workload": wl.name, "ddim_steps": n_steps,
+                      "eta": wl.eta, "unsynchronised_mean_abs_disc_over_steps": float(np.mean(base_traj)),
+                      "unsynchronised_final_mean_abs_disc": base_traj[-1], "rows": rows,
+                      "note": "point-mass stand-in denoiser: every run ends on the reference maps, so final "
+                              "discrepancy and drift do not depend on K"}), flush=True)
 
 
 def cpu_baseline(wl, n_steps, seed, target_s):
@@ -154,6 +236,8 @@ def main():
     if args.copy_only:
         return copy_only(args, wl)
     n_steps = args.n_steps or wl.n_steps[0]
+    if args.sync_ablation:
+        return sync_ablation(args, wl, n_steps)
     dev = torch.device("cuda:0")
     lay = pc.PCLayout(wl.n_regions, wl.n_guidance, wl.n_traj, wl.chain_len, wl.overlap if wl.chain_len > 1 else 0)
     x0c, x0u = reference_maps(wl, args.seed)
