@@ -44,6 +44,8 @@ def parse():
     p.add_argument("--eps-buffers", action="store_true",
                    help="step with noise predictions read from buffers (the interface of a trained denoiser) "
                         "instead of the point-mass stand-in: 16 B per element-step instead of 8")
+    p.add_argument("--graph", action="store_true",
+                   help="capture one pass in a HIP graph and time graph replays (for launch-bound small workloads)")
     p.add_argument("--sync-ablation", default="",
                    help="comma-separated projection intervals K (0 = never) for a sync-frequency ablation on a "
                         "chain workload; prints one JSON line with a row per K")
@@ -275,6 +277,43 @@ def main():
     torch.cuda.synchronize()
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    if args.graph:
+        # three graphs per pass (x_T, the step loop, MDS); the events go between the replays
+        def seg_init():
+            pc.pc_init_state(state, lay, args.seed)
+
+        def seg_steps():
+            if args.eps_buffers:
+                for i in range(n_steps):
+                    pc.pc_ddim_cfg_step_eps(state, eps_c, eps_u, list(wl.w), lay, a_t[i], a_n[i], wl.eta,
+                                            args.seed, i + 1, project_seams=bool(project))
+            else:
+                pc.pc_ddim_sample(state, x0c_d, x0u_d, list(wl.w), lay, n_steps, wl.eta, args.seed,
+                                  project_every=project, init=False)
+
+        def seg_mds():
+            pc.pc_mds_recover(state, coords)
+
+        graphs = []
+        for seg in (seg_init, seg_steps, seg_mds):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                seg()
+            graphs.append(g)
+
+        def one_pass(events=None):  # noqa: F811 - the graph-replay form of the pass
+            graphs[0].replay()
+            if events:
+                events[0].record(stream)
+            graphs[1].replay()
+            if events:
+                events[1].record(stream)
+            graphs[2].replay()
+            if events:
+                events[2].record(stream)
+
+        one_pass()
+        torch.cuda.synchronize()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -305,6 +344,7 @@ def main():
         "config": {"workload": wl.name, "maps": lay.n_maps, "regions": wl.n_regions, "guidance": wl.n_guidance,
                    "trajectories": wl.n_traj, "chain_len": wl.chain_len, "ddim_steps": n_steps, "eta": wl.eta,
                    "seed": args.seed, "denoiser": "noise-prediction buffers" if args.eps_buffers else "point-mass",
+                   "launch": "HIP graph replay" if args.graph else "eager",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "k_step_indep" if wl.chain_len == 1 else "k_step_chain",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
