@@ -5,8 +5,8 @@ import pytest
 
 import tiled_genome_diffusion_amd as pc
 from gpu_util import DIST_RTOL, layout_of, run_steps, say, torch_dev, upload_refs
-from oracle import mds
-from workloads import get, packed_distances, random_walk, walk_rng
+from oracle import layout, mds
+from workloads import get, packed_distances, pseudo_euclidean_map, random_walk, walk_rng
 
 pytestmark = pytest.mark.gpu
 
@@ -88,5 +88,24 @@ def test_non_euclidean_maps():
     maps = np.array(maps, dtype=np.float32)
     coords, eig = gpu_mds(maps, max_iters=256)
     oc, ol = zip(*[mds.classical_mds(m.astype(np.float64)) for m in maps])
+    assert dist_err(coords, oc) <= DIST_RTOL
+    assert np.allclose(eig, np.array(ol), rtol=1e-4, atol=1e-4 * np.abs(np.array(ol)).max())
+
+
+def test_hidden_third_eigenvalue():
+    # Maps whose Gram matrix has negative eigenvalues larger in magnitude than the
+    # third wanted one: a block-4 iteration by magnitude misses lambda_3 and the
+    # solver must deflate the negative directions and iterate again.
+    say("mds on pseudo-Euclidean maps that hide lambda_3")
+    folds = [(1.0, -1.0, 3.0, -4.0), (0.0, 2.0, -2.0, 5.0, -5.0), (1.0, -1.0)]
+    maps = np.array([pseudo_euclidean_map(walk_rng(13, k), folds=folds[k % 3]) for k in range(36)])
+    hidden = 0
+    for m in maps:
+        ev = np.linalg.eigvalsh(mds.double_centre(layout.unpack(m.astype(np.float32).astype(np.float64))))
+        top4 = ev[np.argsort(-np.abs(ev))[:4]]
+        hidden += not np.all(np.isin(np.sort(ev)[::-1][:3], top4))
+    assert hidden >= 20
+    coords, eig = gpu_mds(maps.astype(np.float32), max_iters=256)
+    oc, ol = zip(*[mds.classical_mds(m.astype(np.float32).astype(np.float64)) for m in maps])
     assert dist_err(coords, oc) <= DIST_RTOL
     assert np.allclose(eig, np.array(ol), rtol=1e-4, atol=1e-4 * np.abs(np.array(ol)).max())

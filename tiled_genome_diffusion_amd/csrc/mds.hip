@@ -9,14 +9,17 @@
 //      modified Gram-Schmidt, Z = B Q (Q broadcast from LDS, 256 FMAs per
 //      lane), H = Q^T Z by DPP wavefront reductions, a 4x4 Jacobi eigensolve
 //      (wave-uniform), Ritz vectors V = Q W, Z W = B V and the residuals
-//      ||B V_k - theta_k V_k|| of the three largest.  Stops when those reach
-//      the float32 floor or after max_iters Rayleigh-Ritz steps.  The
-//      workgroup is capped at 128 VGPRs so four maps run per SIMD (the kernel
-//      is VALU-bound; four waves beat three by 12% on MI355X).
-//   4. The iteration finds the eigenvalues of largest magnitude.  If a
-//      negative one could hide a positive eigenvalue (the third largest Ritz
-//      value is below the smallest magnitude found), it reruns on B + mu I
-//      with mu >= -lambda_min, where magnitude order equals algebraic order.
+//      ||B V_k - theta_k V_k|| of the three largest.  Stops when each is
+//      small against its pair's gap (eigenvector error ~ residual / gap) or
+//      after max_iters Rayleigh-Ritz steps.  The workgroup is capped at 128
+//      VGPRs so four maps run per SIMD (the kernel is VALU-bound; four waves
+//      beat three by 12% on MI355X).
+//   4. The iteration finds the eigenvalues of largest magnitude.  If negative
+//      ones could hide a positive eigenvalue (the third largest Ritz value is
+//      below the smallest magnitude found), the negative Ritz vectors that
+//      outrank it are projected out (held in LDS) and the iteration restarts
+//      on the complement, at most kPasses passes in all, so the largest
+//      magnitudes left are the wanted positive eigenvalues.
 //   5. X = V_3 diag(sqrt(max(theta, 0))), each column signed so that its
 //      largest-magnitude entry is positive (lowest index on ties).
 #include "common.hpp"
@@ -115,13 +118,34 @@ __device__ __forceinline__ void orthonormalise(int lane, const float (&y)[kBlk],
     }
 }
 
-// z = (B + mu I) q for the four per-lane columns q (row `lane` of B in b).
-__device__ __forceinline__ void block_matvec(const float (&b)[kBeads], float mu, int lane, const float (&q)[kBlk],
-                                             float4 *s_q, float (&z)[kBlk]) {
+constexpr int kPasses = 4;                     // iteration passes per map, at most
+constexpr int kMaxDefl = (kPasses - 1) * kBlk;  // deflated vectors, at most
+static_assert(kMaxDefl * kBeads <= kPacked, "deflated vectors are kept in the map's LDS buffer");
+
+// Deflated Ritz vectors: n of them in LDS, vector d's component for bead l at
+// v[d * kBeads + l].  They are orthonormal to float32 rounding.
+struct Deflation {
+    float *v;
+    int n;
+};
+
+// Removes from the four per-lane columns z their components along the deflated
+// vectors, one vector after the other.
+__device__ __forceinline__ void project_out(const Deflation &dfl, int lane, float (&z)[kBlk]) {
+    for (int d = 0; d < dfl.n; ++d) {
+        const float v = dfl.v[d * kBeads + lane];
+#pragma unroll
+        for (int k = 0; k < kBlk; ++k) z[k] = fmaf(-wave_sum(v * z[k]), v, z[k]);
+    }
+}
+
+// z = B q for the four per-lane columns q (row `lane` of B in b).
+__device__ __forceinline__ void block_matvec(const float (&b)[kBeads], int lane,
+                                             const float (&q)[kBlk], float4 *s_q, float (&z)[kBlk]) {
     s_q[lane] = make_float4(q[0], q[1], q[2], q[3]);
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < kBlk; ++k) z[k] = mu * q[k];
+    for (int k = 0; k < kBlk; ++k) z[k] = 0.f;
 #pragma unroll
     for (int j = 0; j < kBeads; ++j) {
         const float4 qj = s_q[j];
@@ -136,22 +160,41 @@ __device__ __forceinline__ void block_matvec(const float (&b)[kBeads], float mu,
     __syncthreads();
 }
 
-// Block-4 subspace iteration on B + mu I.  Each iteration orthonormalises
-// the last product (q <- MGS(z), starting from fixed pseudo-random vectors),
-// multiplies again (z <- (B + mu I) q), and from the second product on tests
-// the Rayleigh-Ritz pairs of (q, z): H = q^T z, H = W diag(theta) W^T,
-// vec = q W, residual ||z W - theta vec|| of the three largest.  On return
-// theta (descending, shift included) and vec (lane = bead) hold the last Ritz
-// pairs; the result is the smallest Ritz magnitude.
-__device__ __forceinline__ float subspace(const float (&b)[kBeads], float mu, int32_t max_iters, int lane,
-                                          float4 *s_q, float (&theta)[kBlk], float (&vec)[kBlk]) {
+// True when negative eigenvalues may hide a wanted one: the third largest Ritz
+// value is below the smallest Ritz magnitude, so an eigenvalue the iteration
+// missed (magnitude <= that smallest one) could outrank it.  Below 1e-6 of the
+// largest Ritz value the spectrum is float32 noise and never counts.
+__device__ __forceinline__ bool may_hide(const float (&d)[kBlk], float rho) {
+    return d[2] < rho && rho > 1e-6f * fabsf(d[0]);
+}
+
+// Block-4 subspace iteration on P B P, P the projector onto the complement of
+// the deflated vectors (none at first).  Each iteration orthonormalises the
+// last product (q <- MGS(z), starting from fixed pseudo-random vectors),
+// multiplies again (z <- P B q), and from the second product on takes the
+// Rayleigh-Ritz pairs of (q, z): H = q^T z, H = W diag(theta) W^T, vec = q W,
+// residual ||z W - theta vec||.
+//
+// A pass ends when the three largest pairs have converged (the result), or
+// after max_iters + 1 products.  If negative eigenvalues may hide a wanted
+// one, the pass ends instead once every pair above 1e-3 of the largest
+// magnitude has converged; the negative pairs that outrank the third largest
+// Ritz value are then deflated and a new pass starts on the complement, whose
+// largest magnitudes move toward the wanted positive eigenvalues.  (B has
+// eigenvalue 0 on the all-ones vector, so its third largest eigenvalue is
+// never negative, and projecting directions out, which leaves 0 in their
+// place, cannot change the three largest.)  On return theta (descending) and
+// vec (lane = bead) hold the last Ritz pairs.
+__device__ __forceinline__ void subspace(const float (&b)[kBeads], Deflation &dfl, int32_t max_iters, int lane,
+                                         float4 *s_q, float (&theta)[kBlk], float (&vec)[kBlk]) {
     float q[kBlk], z[kBlk];
 #pragma unroll
     for (int k = 0; k < kBlk; ++k) z[k] = start_vec(lane, k);
-    float rho = 0.f;
-    for (int it = 0; it <= max_iters; ++it) {
+    int pass = 0;
+    for (int it = 0;; ++it) {
         orthonormalise(lane, z, q);
-        block_matvec(b, mu, lane, q, s_q, z);
+        block_matvec(b, lane, q, s_q, z);
+        project_out(dfl, lane, z);
         if (it == 0) continue;  // the first product only seeds the subspace
         float h[kBlk][kBlk], w[kBlk][kBlk];
 #pragma unroll
@@ -181,8 +224,7 @@ __device__ __forceinline__ float subspace(const float (&b)[kBeads], float mu, in
                 }
             }
         float yv[kBlk];
-        float thmax = 0.f;
-        rho = 3.4e38f;
+        float thmax = 0.f, rho = 3.4e38f;
 #pragma unroll
         for (int k = 0; k < kBlk; ++k) {
             vec[k] = q[0] * w[0][k] + q[1] * w[1][k] + q[2] * w[2][k] + q[3] * w[3][k];
@@ -191,18 +233,51 @@ __device__ __forceinline__ float subspace(const float (&b)[kBeads], float mu, in
             thmax = fmaxf(thmax, fabsf(d[k]));
             rho = fminf(rho, fabsf(d[k]));
         }
-        const float tol = 4e-6f * thmax;
+        // A wanted pair has converged when its residual would move its
+        // coordinate column (vec sqrt(theta)) by ~4e-6 of the largest one: an
+        // eigenvector error is about residual / gap, so the tolerance scales
+        // with the pair's gap to the other Ritz values (and, for the third, to
+        // the largest magnitude the block may have missed), clamped to
+        // [5e-7, 4e-6] of the largest magnitude (5e-7: float32 floor).  Pairs
+        // to deflate take 4e-6.
+        const bool hide = may_hide(d, rho);
+        const float cap = 4e-6f * thmax, floor_tol = 5e-7f * thmax;
         bool done = true;
 #pragma unroll
-        for (int k = 0; k < 3; ++k) {
+        for (int k = 0; k < kBlk; ++k) {
+            if (!done || (!hide && k == 3)) break;  // wave-uniform
             const float r = yv[k] - d[k] * vec[k];
-            done = done && wave_sum(r * r) <= tol * tol;
+            const float r2 = wave_sum(r * r);
+            float tk = cap;
+            if (!hide && d[k] > 0.f) {
+                float g = k == 2 ? d[k] - rho : 3.4e38f;
+#pragma unroll
+                for (int j = 0; j < kBlk; ++j)
+                    if (j != k) g = fminf(g, fabsf(d[k] - d[j]));
+                tk = fminf(cap, fmaxf(floor_tol, 4e-6f * fmaxf(g, 0.f) * sqrtf(thmax / d[k])));
+            }
+            if (!hide || fabsf(d[k]) >= 1e-3f * thmax) done = r2 <= tk * tk;
         }
-        if (done) break;
+        if (done || it >= max_iters) {
+            if (!hide || pass == kPasses - 1) break;
+            const float floor = fmaxf(d[2], 0.f);
+#pragma unroll
+            for (int k = 0; k < kBlk; ++k) {
+                if (d[k] < 0.f && -d[k] > floor) {  // wave-uniform
+                    dfl.v[dfl.n * kBeads + lane] = vec[k];
+                    ++dfl.n;
+                }
+            }
+            ++pass;
+            it = -1;
+#pragma unroll
+            for (int k = 0; k < kBlk; ++k) z[k] = start_vec(lane, k);
+            project_out(dfl, lane, z);
+            continue;
+        }
 #pragma unroll
         for (int k = 0; k < kBlk; ++k) z[k] = yv[k];
     }
-    return rho;
 }
 
 __global__ __launch_bounds__(kLanes, 4) void k_mds(const float *__restrict__ maps, float *__restrict__ coords,
@@ -239,19 +314,8 @@ __global__ __launch_bounds__(kLanes, 4) void k_mds(const float *__restrict__ map
     for (int j = 0; j < kBeads; ++j) b[j] = -0.5f * (b[j] - mean_i - s_mean[j] + gmean);
 
     float theta[kBlk], vec[kBlk];
-    const float rho = subspace(b, 0.f, max_iters, i, s_q, theta, vec);
-    // The iteration finds the eigenvalues of largest magnitude; any eigenvalue
-    // it missed has magnitude <= rho.  If the third largest Ritz value is below
-    // rho, a missed positive eigenvalue could outrank it: iterate on B + mu I,
-    // mu >= -lambda_min, where magnitude order is algebraic order.  Below
-    // 1e-6 of the largest Ritz value the spectrum is float32 noise and no
-    // rerun is needed.
-    if (theta[2] < rho && rho > 1e-6f * fabsf(theta[0])) {
-        const float mu = fmaxf(-theta[3], rho);
-        subspace(b, mu, max_iters, i, s_q, theta, vec);
-#pragma unroll
-        for (int k = 0; k < kBlk; ++k) theta[k] -= mu;
-    }
+    Deflation dfl{reinterpret_cast<float *>(s_map), 0};  // the packed map is dead once B is in registers
+    subspace(b, dfl, max_iters, i, s_q, theta, vec);
 
     // Sign each column by its largest-magnitude entry (lowest bead on ties).
     float out[3];

@@ -19,4 +19,4 @@ from .configs import (  # noqa: F401
     reference_maps,
     reference_walks,
 )
-from .walks import packed_distances, random_walk, walk_rng  # noqa: F401
+from .walks import packed_distances, pseudo_euclidean_map, random_walk, walk_rng  # noqa: F401

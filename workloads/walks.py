@@ -46,3 +46,24 @@ def packed_distances(coords: np.ndarray) -> np.ndarray:
     iu, ju = np.triu_indices(n, 1)
     diff = coords[iu] - coords[ju]
     return np.sqrt(np.einsum("ij,ij->i", diff, diff))
+
+
+def pseudo_euclidean_map(rng: np.random.Generator, n_beads: int = 64, folds=(1.0, -1.0), fold_scale: float = 0.8,
+                         spread=(0.6, 0.5)) -> np.ndarray:
+    """A packed map that no 3D point set realises, with large negative directions.
+
+    Beads sit along a noisy line (x, plus two small Gaussian coordinates); each
+    entry of ``folds`` adds a coordinate fold_scale * |x - c| whose squared
+    differences are subtracted instead of added (a pseudo-Euclidean space of
+    signature (3, len(folds))).  Squared distances below zero are clamped.  The
+    double-centred Gram matrix of such a map has, besides its three wanted
+    positive eigenvalues, negative ones larger in magnitude than the second and
+    third: the case where an eigen-solver that ranks by magnitude can miss a
+    wanted eigenvalue.
+    """
+    x1 = np.linspace(-10.0, 10.0, n_beads) + rng.normal(0.0, 0.05, n_beads)
+    pos = np.stack([x1, rng.normal(0.0, spread[0], n_beads), rng.normal(0.0, spread[1], n_beads)], 1)
+    neg = np.stack([fold_scale * np.abs(x1 - c) for c in folds], 1)
+    iu, ju = np.triu_indices(n_beads, 1)
+    d2 = ((pos[iu] - pos[ju]) ** 2).sum(1) - ((neg[iu] - neg[ju]) ** 2).sum(1)
+    return np.sqrt(np.maximum(d2, 0.0))
