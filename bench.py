@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--sync-ablation", default="",
                    help="comma-separated projection intervals K (0 = never) for a sync-frequency ablation on a "
                         "chain workload; prints one JSON line with a row per K")
+    p.add_argument("--traffic-summary", default="", metavar="PMC_DIR",
+                   help="no GPU: turn the FETCH_SIZE / WRITE_SIZE counter runs under PMC_DIR (copy_<C>/ and "
+                        "slab_<C>/ rocprofv3 csv output) into profiles/k_step_indep_<workload>_traffic.json")
     p.add_argument("--copy-only", action="store_true",
                    help="time a plain device-to-device copy of the workload's state size instead "
                         "(the calibration kernel for the HBM byte counters)")
@@ -65,12 +68,64 @@ def measured_traffic(workload: str):
         if d.get("workload") != workload:
             continue
         h = hashlib.sha256()
-        for rel in d["source_files"]:
+        for rel in d["source_files"]:  # the files the counters were taken on
             with open(os.path.join(ROOT, rel), "rb") as f:
                 h.update(f.read())
         if h.hexdigest() == d["source_sha256"]:
             return d["traffic_bytes_per_launch"], d["kernel"]
     return None, None
+
+
+STEP_SOURCES = ["tiled_genome_diffusion_amd/csrc/step.hip", "tiled_genome_diffusion_amd/csrc/common.hpp"]
+
+
+def traffic_summary(args, wl):
+    """Scale the step kernel's FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what the
+    same counters read for the plain copy of bench.py --copy-only, and store the
+    result with the hash of the kernel source it was measured on."""
+    import csv
+
+    def per_kernel(run, counter):
+        path = glob.glob(os.path.join(args.traffic_summary, f"{run}_{counter}", "*_counter_collection.csv"))[0]
+        acc = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+    copy_bytes = wl.n_maps * 2016 * 4
+    scale = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        kib = max(per_kernel("copy", c).values())[0]   # the copy dispatch dominates the run
+        scale[c] = (kib, copy_bytes / 1024.0 / kib)
+    fetch, write = per_kernel("slab", "FETCH_SIZE"), per_kernel("slab", "WRITE_SIZE")
+    name = max((k for k in fetch if "k_step_indep" in k), key=lambda k: fetch[k][1])   # the noisy-step form
+    h = hashlib.sha256()
+    for rel in STEP_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    rd = fetch[name][0] * 1024 * scale["FETCH_SIZE"][1]
+    wr = write[name][0] * 1024 * scale["WRITE_SIZE"][1]
+    def short(k):
+        return k.replace("void ", "").replace("pc::(anonymous namespace)::", "").split("(")[0]
+
+    out = {"kernel": short(name), "workload": wl.name,
+           "source_files": STEP_SOURCES, "source_sha256": h.hexdigest(),
+           "fetch_size_kib_per_launch": fetch[name][0], "write_size_kib_per_launch": write[name][0],
+           "launches_averaged": fetch[name][1],
+           "copy_fetch_size_kib": scale["FETCH_SIZE"][0], "copy_write_size_kib": scale["WRITE_SIZE"][0],
+           "copy_bytes": copy_bytes, "fetch_scale": scale["FETCH_SIZE"][1], "write_scale": scale["WRITE_SIZE"][1],
+           "traffic_bytes_per_launch": rd + wr, "fetch_bytes_per_launch": rd, "write_bytes_per_launch": wr,
+           "algorithmic_read_bytes": wl.n_maps * 2016 * 4 + wl.n_regions * REF_BYTES_PER_REGION,
+           "algorithmic_write_bytes": wl.n_maps * 2016 * 4}
+    with open(os.path.join(ROOT, "profiles", f"k_step_indep_{wl.name}_traffic.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    for k in sorted(fetch):
+        fr, wr_ = fetch[k][0], write.get(k, (float("nan"), 0))[0]
+        print(f"| `{short(k)}` (avg of {fetch[k][1]}) | {fr:,.0f} | {wr_:,.0f} | "
+              f"{fr * 1024 * scale['FETCH_SIZE'][1]:,.0f} | {wr_ * 1024 * scale['WRITE_SIZE'][1]:,.0f} |")
+    print(json.dumps(out, indent=1))
 
 
 def copy_only(args, wl):
@@ -235,6 +290,8 @@ def main():
     from workloads import get, reference_maps
 
     wl = get(args.workload)
+    if args.traffic_summary:
+        return traffic_summary(args, wl)
     if args.copy_only:
         return copy_only(args, wl)
     n_steps = args.n_steps or wl.n_steps[0]
