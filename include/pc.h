@@ -219,13 +219,16 @@ PC_API pc_status pc_seam_mean_abs(const float *state, const pc_layout *layout, f
  * B = -1/2 J (D o D) J, its three largest eigenpairs by block subspace
  * iteration (block 4, Rayleigh-Ritz), negative eigenvalues clamped to zero,
  * X = V_3 diag(sqrt(lambda)).  Each column of X is signed so that its
- * largest-magnitude entry is positive.  Exact whenever the three largest
- * eigenvalues are among the four of largest magnitude (always for maps that
- * are Euclidean up to rounding).
+ * largest-magnitude entry is positive.  The iteration ranks by magnitude; when
+ * large negative eigenvalues (a map far from Euclidean) could hide one of the
+ * three wanted ones, their directions are projected out and the iteration
+ * restarts, up to four passes.
  *   maps      device float [n_maps][2016].
  *   coords    device float [n_maps][64][3], written.
  *   eigvals   device float [n_maps][3] or NULL: the three eigenvalues, descending.
- *   max_iters iteration cap, 1..256 (0 selects 32).
+ *   max_iters cap on the Rayleigh-Ritz steps of a map over all passes, 1..256
+ *             (0 selects 128).  Maps that are Euclidean up to rounding take 1-4;
+ *             the cap is reached only by maps far from any point cloud.
  * Errors: NULL maps/coords; n_maps < 0 or overflowing; max_iters out of range.
  * n_maps = 0 is a no-op.
  */

@@ -109,3 +109,13 @@ def test_hidden_third_eigenvalue():
     oc, ol = zip(*[mds.classical_mds(m.astype(np.float32).astype(np.float64)) for m in maps])
     assert dist_err(coords, oc) <= DIST_RTOL
     assert np.allclose(eig, np.array(ol), rtol=1e-4, atol=1e-4 * np.abs(np.array(ol)).max())
+
+
+def test_hidden_third_eigenvalue_default_budget():
+    # the same maps with the default iteration budget
+    say("mds on pseudo-Euclidean maps, default budget")
+    folds = [(1.0, -1.0, 3.0, -4.0), (0.0, 2.0, -2.0, 5.0, -5.0), (1.0, -1.0)]
+    maps = np.array([pseudo_euclidean_map(walk_rng(13, k), folds=folds[k % 3]) for k in range(36)], dtype=np.float32)
+    coords, _ = gpu_mds(maps)
+    oc = [mds.classical_mds(m.astype(np.float64))[0] for m in maps]
+    assert dist_err(coords, oc) <= DIST_RTOL

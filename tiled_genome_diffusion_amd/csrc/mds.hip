@@ -11,9 +11,9 @@
 //      (wave-uniform), Ritz vectors V = Q W, Z W = B V and the residuals
 //      ||B V_k - theta_k V_k|| of the three largest.  Stops when each is
 //      small against its pair's gap (eigenvector error ~ residual / gap) or
-//      after max_iters Rayleigh-Ritz steps.  The workgroup is capped at 128
-//      VGPRs so four maps run per SIMD (the kernel is VALU-bound; four waves
-//      beat three by 12% on MI355X).
+//      after max_iters Rayleigh-Ritz steps in all.  The workgroup is capped
+//      at 128 VGPRs so four maps run per SIMD (the kernel is VALU-bound; four
+//      waves beat three by 12% on MI355X).
 //   4. The iteration finds the eigenvalues of largest magnitude.  If negative
 //      ones could hide a positive eigenvalue (the third largest Ritz value is
 //      below the smallest magnitude found), the negative Ritz vectors that
@@ -175,12 +175,13 @@ __device__ __forceinline__ bool may_hide(const float (&d)[kBlk], float rho) {
 // Rayleigh-Ritz pairs of (q, z): H = q^T z, H = W diag(theta) W^T, vec = q W,
 // residual ||z W - theta vec||.
 //
-// A pass ends when the three largest pairs have converged (the result), or
-// after max_iters + 1 products.  If negative eigenvalues may hide a wanted
-// one, the pass ends instead once every pair above 1e-3 of the largest
-// magnitude has converged; the negative pairs that outrank the third largest
-// Ritz value are then deflated and a new pass starts on the complement, whose
-// largest magnitudes move toward the wanted positive eigenvalues.  (B has
+// A pass ends when the three largest pairs have converged (the result).  If
+// negative eigenvalues may hide a wanted one, it ends instead once every pair
+// above 1e-3 of the largest magnitude has converged; the negative pairs that
+// outrank the third largest Ritz value are then deflated and a new pass
+// starts on the complement, whose largest magnitudes move toward the wanted
+// positive eigenvalues.  The whole iteration stops after max_iters
+// Rayleigh-Ritz steps over all passes.  (B has
 // eigenvalue 0 on the all-ones vector, so its third largest eigenvalue is
 // never negative, and projecting directions out, which leaves 0 in their
 // place, cannot change the three largest.)  On return theta (descending) and
@@ -190,7 +191,7 @@ __device__ __forceinline__ void subspace(const float (&b)[kBeads], Deflation &df
     float q[kBlk], z[kBlk];
 #pragma unroll
     for (int k = 0; k < kBlk; ++k) z[k] = start_vec(lane, k);
-    int pass = 0;
+    int pass = 0, steps = 0;
     for (int it = 0;; ++it) {
         orthonormalise(lane, z, q);
         block_matvec(b, lane, q, s_q, z);
@@ -258,8 +259,9 @@ __device__ __forceinline__ void subspace(const float (&b)[kBeads], Deflation &df
             }
             if (!hide || fabsf(d[k]) >= 1e-3f * thmax) done = r2 <= tk * tk;
         }
-        if (done || it >= max_iters) {
-            if (!hide || pass == kPasses - 1) break;
+        const bool spent = ++steps >= max_iters;
+        if (done || spent) {
+            if (!hide || pass == kPasses - 1 || spent) break;
             const float floor = fmaxf(d[2], 0.f);
 #pragma unroll
             for (int k = 0; k < kBlk; ++k) {
