@@ -166,11 +166,8 @@ def sync_ablation(args, wl, n_steps):
     state = torch.empty(lay.n_maps * pc.PACKED, dtype=torch.float32, device=dev)
     disc = torch.empty(lay.n_seams * lay.n_guidance, dtype=torch.float32, device=dev)
     a_t, a_n = pc.pc_ddim_schedule(n_steps)
-    li, ri = [], []
-    for p_, q_ in [(p_, q_) for p_ in range(wl.overlap) for q_ in range(p_ + 1, wl.overlap)]:
-        off = 64 - wl.overlap
-        li.append((off + p_) * (127 - (off + p_)) // 2 + (off + q_ - (off + p_) - 1))
-        ri.append(p_ * (127 - p_) // 2 + (q_ - p_ - 1))
+    seam_map = pc.pc_seam_index_map(wl.overlap)   # packed index of each shared pair in the left / right tile
+    li, ri = seam_map[:, 0], seam_map[:, 1]
     keep = np.ones((wl.chain_len, pc.PACKED), dtype=bool)
     keep[:-1, li] = False
     keep[1:, ri] = False
