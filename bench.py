@@ -34,11 +34,13 @@ REF_BYTES_PER_REGION = 2016 * 4 * 2  # conditional + unconditional reference, on
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=5, help="timed passes")
+    p.add_argument("--steps", type=int, default=6, help="timed passes")
     p.add_argument("--warmup", type=int, default=1, help="untimed passes")
     p.add_argument("--workload", default="genome_slab")
     p.add_argument("--n-steps", type=int, default=0, help="DDIM steps (default: the workload's first)")
-    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--seed", type=int, default=0, help="seed of the ablation and cpu baseline")
+    p.add_argument("--seeds", default="0,1,2",
+                   help="base seeds the timed passes cycle through (inputs and noise); per-seed rates are reported")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target duration of the oracle baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--eps-buffers", action="store_true",
@@ -270,7 +272,19 @@ def cpu_baseline(wl, n_steps, seed, target_s):
             "sample": f"{n_maps} of {wl.n_maps} maps ({wl.name}), {n_steps} float64 DDIM steps + LAPACK MDS, "
                       f"one thread; {ts:.1f} s sampling + {tm:.1f} s MDS",
             "mds_maps_per_s": n_maps / tm, "step_traj_steps_per_s": n_maps * n_steps / ts,
-            "host_cpu_count": os.cpu_count(), "host_affinity": len(os.sched_getaffinity(0))}
+            "host_cpu_count": os.cpu_count(), "host_affinity": len(os.sched_getaffinity(0)),
+            "host_cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
@@ -296,29 +310,36 @@ def main():
         return sync_ablation(args, wl, n_steps)
     dev = torch.device("cuda:0")
     lay = pc.PCLayout(wl.n_regions, wl.n_guidance, wl.n_traj, wl.chain_len, wl.overlap if wl.chain_len > 1 else 0)
-    x0c, x0u = reference_maps(wl, args.seed)
-    x0c_d, x0u_d = torch.from_numpy(x0c).to(dev), torch.from_numpy(x0u).to(dev)
+    seeds = [int(v) for v in args.seeds.split(",")]
+    if args.graph:
+        seeds = seeds[:1]   # a captured graph holds one seed
+    refs = {}
+    for sd in seeds:
+        x0c, x0u = reference_maps(wl, sd)
+        refs[sd] = (torch.from_numpy(x0c).to(dev), torch.from_numpy(x0u).to(dev))
     state = torch.empty(lay.n_maps * pc.PACKED, dtype=torch.float32, device=dev)
     coords = torch.empty(lay.n_maps * 64 * 3, dtype=torch.float32, device=dev)
     project = 1 if wl.chain_len > 1 else 0
     stream = torch.cuda.current_stream(dev)
     if args.eps_buffers:
         # stand-ins for a network's per-map outputs, drawn once; each step reads both
-        gen = torch.Generator(device=dev).manual_seed(args.seed)
+        gen = torch.Generator(device=dev).manual_seed(seeds[0])
         eps_c = torch.randn(lay.n_maps * pc.PACKED, generator=gen, device=dev)
         eps_u = torch.randn(lay.n_maps * pc.PACKED, generator=gen, device=dev)
         a_t, a_n = pc.pc_ddim_schedule(n_steps)
 
-    def one_pass(events=None):
-        pc.pc_init_state(state, lay, args.seed)
+    def one_pass(events=None, sd=seeds[0]):
+        if events:
+            events[3].record(stream)
+        pc.pc_init_state(state, lay, sd)
         if events:
             events[0].record(stream)
         if args.eps_buffers:
             for i in range(n_steps):
-                pc.pc_ddim_cfg_step_eps(state, eps_c, eps_u, list(wl.w), lay, a_t[i], a_n[i], wl.eta, args.seed,
+                pc.pc_ddim_cfg_step_eps(state, eps_c, eps_u, list(wl.w), lay, a_t[i], a_n[i], wl.eta, sd,
                                         i + 1, project_seams=bool(project))
         else:
-            pc.pc_ddim_sample(state, x0c_d, x0u_d, list(wl.w), lay, n_steps, wl.eta, args.seed,
+            pc.pc_ddim_sample(state, refs[sd][0], refs[sd][1], list(wl.w), lay, n_steps, wl.eta, sd,
                               project_every=project, init=False)
         if events:
             events[1].record(stream)
@@ -326,23 +347,26 @@ def main():
         if events:
             events[2].record(stream)
 
-    for _ in range(args.warmup):
-        one_pass()
+    for k in range(args.warmup):
+        one_pass(sd=seeds[k % len(seeds)])
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # events per pass: [0] after x_T, [1] after the step loop, [2] after MDS, [3] before x_T
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     if args.graph:
         # three graphs per pass (x_T, the step loop, MDS); the events go between the replays
+        sd0 = seeds[0]
+
         def seg_init():
-            pc.pc_init_state(state, lay, args.seed)
+            pc.pc_init_state(state, lay, sd0)
 
         def seg_steps():
             if args.eps_buffers:
                 for i in range(n_steps):
                     pc.pc_ddim_cfg_step_eps(state, eps_c, eps_u, list(wl.w), lay, a_t[i], a_n[i], wl.eta,
-                                            args.seed, i + 1, project_seams=bool(project))
+                                            sd0, i + 1, project_seams=bool(project))
             else:
-                pc.pc_ddim_sample(state, x0c_d, x0u_d, list(wl.w), lay, n_steps, wl.eta, args.seed,
+                pc.pc_ddim_sample(state, refs[sd0][0], refs[sd0][1], list(wl.w), lay, n_steps, wl.eta, sd0,
                                   project_every=project, init=False)
 
         def seg_mds():
@@ -355,7 +379,9 @@ def main():
                 seg()
             graphs.append(g)
 
-        def one_pass(events=None):  # noqa: F811 - the graph-replay form of the pass
+        def one_pass(events=None, sd=sd0):  # noqa: F811 - the graph-replay form of the pass
+            if events:
+                events[3].record(stream)
             graphs[0].replay()
             if events:
                 events[0].record(stream)
@@ -371,9 +397,28 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        one_pass(evs[k])
+        one_pass(evs[k], seeds[k % len(seeds)])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+
+    # per-seed rates from the GPU time of each pass (x_T + steps + MDS)
+    traj_steps = lay.n_maps * n_steps
+    per_seed = {}
+    for k, e in enumerate(evs):
+        per_seed.setdefault(seeds[k % len(seeds)], []).append(e[3].elapsed_time(e[2]))
+    by_seed = {str(sd): traj_steps / (float(np.mean(v)) * 1e-3) for sd, v in per_seed.items()}
+
+    # the same bytes moved by a plain device-to-device copy (read + write of the state size)
+    dst = torch.empty_like(state)
+    dst.copy_(state)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(5):
+        dst.copy_(state)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * state.numel() * 4 / (c0.elapsed_time(c1) / 5 * 1e-3) / 1e9
+    del dst
 
     ms_per_pass = (t1 - t0) * 1e3 / args.steps
     step_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
@@ -384,7 +429,6 @@ def main():
     else:
         bytes_per_launch = lay.n_maps * STEP_BYTES_PER_MAP + lay.n_regions * REF_BYTES_PER_REGION
     achieved = bytes_per_launch / (launch_ms * 1e-3) / 1e9
-    traj_steps = lay.n_maps * n_steps
     traffic, traffic_kernel = measured_traffic(wl.name) if not args.eps_buffers else (None, None)
 
     out = {
@@ -397,14 +441,17 @@ def main():
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": wl.name, "maps": lay.n_maps, "regions": wl.n_regions, "guidance": wl.n_guidance,
                    "trajectories": wl.n_traj, "chain_len": wl.chain_len, "ddim_steps": n_steps, "eta": wl.eta,
-                   "seed": args.seed, "denoiser": "noise-prediction buffers" if args.eps_buffers else "point-mass",
+                   "seeds": seeds, "denoiser": "noise-prediction buffers" if args.eps_buffers else "point-mass",
                    "launch": "HIP graph replay" if args.graph else "eager",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "k_step_indep" if wl.chain_len == 1 else "k_step_chain",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "traffic_unit": "bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-scaled)",
                      "traffic_kernel": traffic_kernel, "launch_us": launch_ms * 1e3,
-                     "bytes_per_launch": bytes_per_launch},
+                     "bytes_per_launch": bytes_per_launch,
+                     "copy_ceiling": copy_gbs, "frac_of_copy": achieved / copy_gbs},
+        "value_by_seed": by_seed,
+        "value_sd_over_seeds": float(np.std(list(by_seed.values()), ddof=1)) if len(by_seed) > 1 else None,
         "step_loop_traj_steps_per_s": traj_steps / (step_ms * 1e-3),
         "mds_maps_per_s": lay.n_maps / (mds_ms * 1e-3),
         "mds_ms": mds_ms,
