@@ -47,13 +47,15 @@ __device__ __forceinline__ float start_vec(int i, int k) {
 // th = (h_qq - h_pp) / (2 h_pq), c = 1 / sqrt(1 + t^2), s = t c; only the
 // entries it changes are updated (h_pp -= t h_pq, h_qq += t h_pq, rows r != p,
 // q rotate).  t needs no correct rounding: c and s are formed from it, so the
-// rotation stays orthogonal, and the hardware rcp / rsq / sqrt are used.  On
-// return h is diagonal to float32 precision and w holds the eigenvectors as
-// columns.
+// rotation stays orthogonal, and the hardware rcp / rsq / sqrt are used.  The
+// eigenvector matrix W is spread over lanes: lane r < 4 holds row r in wl, so
+// a rotation costs each lane two columns of one row.  Rotations whose h_pq^2
+// is below `skip2` (1e-15 of the squared diagonal norm, under float32
+// resolution of the largest eigenvalue) are skipped.
 template <int P, int Q>
-__device__ __forceinline__ void jacobi_rotate(float (&h)[kBlk][kBlk], float (&w)[kBlk][kBlk]) {
+__device__ __forceinline__ void jacobi_rotate(float (&h)[kBlk][kBlk], float (&wl)[kBlk], float skip2) {
     const float apq = h[P][Q];
-    if (apq == 0.f) return;
+    if (apq * apq <= skip2) return;  // wave-uniform
     const float th = (h[Q][Q] - h[P][P]) * 0.5f * __builtin_amdgcn_rcpf(apq);
     const float at = fabsf(th);
     const float t = at > 1e18f ? 0.5f * __builtin_amdgcn_rcpf(th)
@@ -70,43 +72,61 @@ __device__ __forceinline__ void jacobi_rotate(float (&h)[kBlk][kBlk], float (&w)
         h[r][P] = h[P][r] = c * hp - sn * hq;
         h[r][Q] = h[Q][r] = sn * hp + c * hq;
     }
-#pragma unroll
-    for (int r = 0; r < kBlk; ++r) {
-        const float wp = w[r][P], wq = w[r][Q];
-        w[r][P] = c * wp - sn * wq;
-        w[r][Q] = sn * wp + c * wq;
-    }
+    const float wp = wl[P], wq = wl[Q];
+    wl[P] = c * wp - sn * wq;
+    wl[Q] = sn * wp + c * wq;
 }
 
-__device__ __forceinline__ void jacobi4(float (&h)[kBlk][kBlk], float (&w)[kBlk][kBlk]) {
+// On return h is diagonal to float32 precision and lane r < 4 holds row r of
+// the eigenvector matrix (eigenvectors as columns) in wl.
+__device__ __forceinline__ void jacobi4(float (&h)[kBlk][kBlk], float (&wl)[kBlk], int lane) {
 #pragma unroll
-    for (int r = 0; r < kBlk; ++r)
-#pragma unroll
-        for (int c = 0; c < kBlk; ++c) w[r][c] = r == c ? 1.f : 0.f;
+    for (int c = 0; c < kBlk; ++c) wl[c] = lane == c ? 1.f : 0.f;
     for (int sweep = 0; sweep < 8; ++sweep) {
         const float off = h[0][1] * h[0][1] + h[0][2] * h[0][2] + h[0][3] * h[0][3] + h[1][2] * h[1][2] +
                           h[1][3] * h[1][3] + h[2][3] * h[2][3];
         const float dia = h[0][0] * h[0][0] + h[1][1] * h[1][1] + h[2][2] * h[2][2] + h[3][3] * h[3][3];
         if (off <= 1e-14f * dia) break;
-        jacobi_rotate<0, 1>(h, w);
-        jacobi_rotate<0, 2>(h, w);
-        jacobi_rotate<0, 3>(h, w);
-        jacobi_rotate<1, 2>(h, w);
-        jacobi_rotate<1, 3>(h, w);
-        jacobi_rotate<2, 3>(h, w);
+        const float skip2 = 1e-15f * dia;
+        jacobi_rotate<0, 1>(h, wl, skip2);
+        jacobi_rotate<0, 2>(h, wl, skip2);
+        jacobi_rotate<0, 3>(h, wl, skip2);
+        jacobi_rotate<1, 2>(h, wl, skip2);
+        jacobi_rotate<1, 3>(h, wl, skip2);
+        jacobi_rotate<2, 3>(h, wl, skip2);
     }
 }
 
+// Largest value over the wavefront of a non-negative v (DPP, as wave_sum).
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+    v = fmaxf(v, dpp<0xB1>(v));
+    v = fmaxf(v, dpp<0x4E>(v));
+    v = fmaxf(v, dpp<0x141>(v));
+    v = fmaxf(v, dpp<0x140>(v));
+    v = fmaxf(v, dpp<0x142, 0xA>(v));
+    v = fmaxf(v, dpp<0x143, 0xC>(v));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 // Modified Gram-Schmidt of the four per-lane columns y into q.  A column that
-// vanishes is replaced by its start vector.
+// loses more than 4 decimal digits of its norm to the projections (the fourth
+// column of B Q when B has rank 3) is projected a second time, which restores
+// orthogonality to float32 precision; a column that vanishes is replaced by
+// its start vector.
 __device__ __forceinline__ void orthonormalise(int lane, const float (&y)[kBlk], float (&q)[kBlk]) {
 #pragma unroll
     for (int k = 0; k < kBlk; ++k) {
         float v = y[k];
         for (int attempt = 0; attempt < 2; ++attempt) {
+            const float n0 = k > 0 ? wave_sum(v * v) : 0.f;
 #pragma unroll
             for (int l = 0; l < k; ++l) v -= wave_sum(q[l] * v) * q[l];
-            const float n2 = wave_sum(v * v);
+            float n2 = wave_sum(v * v);
+            if (k > 0 && n2 < 1e-4f * n0) {  // cancellation: project once more
+#pragma unroll
+                for (int l = 0; l < k; ++l) v -= wave_sum(q[l] * v) * q[l];
+                n2 = wave_sum(v * v);
+            }
             if (n2 > 1e-30f) {
                 v *= __builtin_amdgcn_rsqf(n2);
                 break;
@@ -197,7 +217,7 @@ __device__ __forceinline__ void subspace(const float (&b)[kBeads], Deflation &df
         block_matvec(b, lane, q, s_q, z);
         project_out(dfl, lane, z);
         if (it == 0) continue;  // the first product only seeds the subspace
-        float h[kBlk][kBlk], w[kBlk][kBlk];
+        float h[kBlk][kBlk], wl[kBlk];
 #pragma unroll
         for (int r = 0; r < kBlk; ++r)
 #pragma unroll
@@ -206,7 +226,7 @@ __device__ __forceinline__ void subspace(const float (&b)[kBeads], Deflation &df
                 h[r][c] = sm;
                 h[c][r] = sm;
             }
-        jacobi4(h, w);
+        jacobi4(h, wl, lane);
         float d[kBlk] = {h[0][0], h[1][1], h[2][2], h[3][3]};
         // Sort descending, carrying the eigenvector columns (selects only).
 #pragma unroll
@@ -217,13 +237,16 @@ __device__ __forceinline__ void subspace(const float (&b)[kBeads], Deflation &df
                 const float t = d[y];
                 d[y] = sw ? d[y + 1] : d[y];
                 d[y + 1] = sw ? t : d[y + 1];
-#pragma unroll
-                for (int r = 0; r < kBlk; ++r) {
-                    const float u = w[r][y];
-                    w[r][y] = sw ? w[r][y + 1] : u;
-                    w[r][y + 1] = sw ? u : w[r][y + 1];
-                }
+                const float u = wl[y];
+                wl[y] = sw ? wl[y + 1] : u;
+                wl[y + 1] = sw ? u : wl[y + 1];
             }
+        // W to every lane (row r from lane r).
+        float w[kBlk][kBlk];
+#pragma unroll
+        for (int r = 0; r < kBlk; ++r)
+#pragma unroll
+            for (int c = 0; c < kBlk; ++c) w[r][c] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl[c]), r));
         float yv[kBlk];
         float thmax = 0.f, rho = 3.4e38f;
 #pragma unroll
@@ -286,7 +309,7 @@ __global__ __launch_bounds__(kLanes, 4) void k_mds(const float *__restrict__ map
                                                 float *__restrict__ eigvals, int32_t max_iters) {
     __shared__ float4 s_map[kQuads];
     __shared__ float4 s_q[kBeads];
-    __shared__ float s_mean[kBeads];
+    __shared__ __align__(16) float s_mean[kBeads];
     const int i = threadIdx.x;
     const size_t m = blockIdx.x;
 
@@ -295,25 +318,42 @@ __global__ __launch_bounds__(kLanes, 4) void k_mds(const float *__restrict__ map
     __syncthreads();
     const float *xs = reinterpret_cast<const float *>(s_map);
 
-    // Row i of A = D o D.
+    // Row i of A = D o D.  Entry (i, j) is packed (i, j) for j > i, i.e.
+    // row[j - 1] of lane i's contiguous packed row, and packed (j, i) for j < i,
+    // i.e. col[c_j] with c_j = idx(j, j + 1) - j - 1; both are reads at a
+    // per-lane base plus a constant offset, and a select keeps the valid one.
+    // Every read stays inside the 2016 entries.
     float b[kBeads];
-    const int base_i = packed_index(i, i + 1) - i - 1;  // idx(i, j) = base_i + j for j > i
+    const float *row = xs + packed_index(i, i + 1) - i;
+    const float *col = xs + i;
     float rsum = 0.f;
 #pragma unroll
     for (int j = 0; j < kBeads; ++j) {
-        const int cj = packed_index(j, j + 1) - j - 1;  // idx(j, i) = cj + i for j < i
-        int addr = j < i ? cj + i : base_i + j;
-        addr = j == i ? 0 : addr;
-        const float d = xs[addr];
+        float d;
+        if (j == 0) {
+            d = xs[i > 0 ? i - 1 : 0];  // packed (0, i) = i - 1
+        } else {
+            const float dr = row[j - 1];
+            const float dc = col[packed_index(j, j + 1) - j - 1];
+            d = j < i ? dc : dr;
+        }
         b[j] = j == i ? 0.f : d * d;
         rsum += b[j];
     }
-    s_mean[i] = rsum * (1.f / kBeads);
+    // B = -1/2 J A J: b_ij = -a_ij / 2 + u_i + u_j with u_i = mean_i / 2 - grand mean / 4.
     const float gmean = wave_sum(rsum) * (1.f / (kBeads * kBeads));
+    const float u_i = 0.5f * (rsum * (1.f / kBeads)) - 0.25f * gmean;
+    s_mean[i] = u_i;
     __syncthreads();
-    const float mean_i = s_mean[i];
+    const float4 *s_u = reinterpret_cast<const float4 *>(s_mean);
 #pragma unroll
-    for (int j = 0; j < kBeads; ++j) b[j] = -0.5f * (b[j] - mean_i - s_mean[j] + gmean);
+    for (int j4 = 0; j4 < kBeads / 4; ++j4) {
+        const float4 u = s_u[j4];
+        b[4 * j4 + 0] = fmaf(b[4 * j4 + 0], -0.5f, u_i + u.x);
+        b[4 * j4 + 1] = fmaf(b[4 * j4 + 1], -0.5f, u_i + u.y);
+        b[4 * j4 + 2] = fmaf(b[4 * j4 + 2], -0.5f, u_i + u.z);
+        b[4 * j4 + 3] = fmaf(b[4 * j4 + 3], -0.5f, u_i + u.w);
+    }
 
     float theta[kBlk], vec[kBlk];
     Deflation dfl{reinterpret_cast<float *>(s_map), 0};  // the packed map is dead once B is in registers
@@ -323,18 +363,10 @@ __global__ __launch_bounds__(kLanes, 4) void k_mds(const float *__restrict__ map
     float out[3];
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
-        float best = fabsf(vec[k]);
-        int arg = i;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            const float ob = __shfl_xor(best, o);
-            const int oa = __shfl_xor(arg, o);
-            if (ob > best || (ob == best && oa < arg)) {
-                best = ob;
-                arg = oa;
-            }
-        }
-        const float sv = __shfl(vec[k], arg);
+        const float a = fabsf(vec[k]);
+        const float best = wave_max_nonneg(a);
+        const int first = __builtin_ctzll(__ballot(a == best));
+        const float sv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vec[k]), first));
         out[k] = (sv < 0.f ? -vec[k] : vec[k]) * sqrtf(fmaxf(theta[k], 0.f));
     }
     float *dst = coords + (m * kBeads + i) * 3;
