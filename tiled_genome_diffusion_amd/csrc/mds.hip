@@ -69,12 +69,12 @@ __device__ __forceinline__ void jacobi_rotate(float (&h)[kBlk][kBlk], float (&wl
     for (int r = 0; r < kBlk; ++r) {
         if (r == P || r == Q) continue;
         const float hp = h[r][P], hq = h[r][Q];
-        h[r][P] = h[P][r] = c * hp - sn * hq;
-        h[r][Q] = h[Q][r] = sn * hp + c * hq;
+        h[r][P] = h[P][r] = fmaf(c, hp, -sn * hq);
+        h[r][Q] = h[Q][r] = fmaf(sn, hp, c * hq);
     }
     const float wp = wl[P], wq = wl[Q];
-    wl[P] = c * wp - sn * wq;
-    wl[Q] = sn * wp + c * wq;
+    wl[P] = fmaf(c, wp, -sn * wq);
+    wl[Q] = fmaf(sn, wp, c * wq);
 }
 
 // On return h is diagonal to float32 precision and lane r < 4 holds row r of
@@ -83,9 +83,15 @@ __device__ __forceinline__ void jacobi4(float (&h)[kBlk][kBlk], float (&wl)[kBlk
 #pragma unroll
     for (int c = 0; c < kBlk; ++c) wl[c] = lane == c ? 1.f : 0.f;
     for (int sweep = 0; sweep < 8; ++sweep) {
-        const float off = h[0][1] * h[0][1] + h[0][2] * h[0][2] + h[0][3] * h[0][3] + h[1][2] * h[1][2] +
-                          h[1][3] * h[1][3] + h[2][3] * h[2][3];
-        const float dia = h[0][0] * h[0][0] + h[1][1] * h[1][1] + h[2][2] * h[2][2] + h[3][3] * h[3][3];
+        float off = h[0][1] * h[0][1], dia = h[0][0] * h[0][0];
+        off = fmaf(h[0][2], h[0][2], off);
+        off = fmaf(h[0][3], h[0][3], off);
+        off = fmaf(h[1][2], h[1][2], off);
+        off = fmaf(h[1][3], h[1][3], off);
+        off = fmaf(h[2][3], h[2][3], off);
+        dia = fmaf(h[1][1], h[1][1], dia);
+        dia = fmaf(h[2][2], h[2][2], dia);
+        dia = fmaf(h[3][3], h[3][3], dia);
         if (off <= 1e-14f * dia) break;
         const float skip2 = 1e-15f * dia;
         jacobi_rotate<0, 1>(h, wl, skip2);
@@ -120,11 +126,11 @@ __device__ __forceinline__ void orthonormalise(int lane, const float (&y)[kBlk],
         for (int attempt = 0; attempt < 2; ++attempt) {
             const float n0 = k > 0 ? wave_sum(v * v) : 0.f;
 #pragma unroll
-            for (int l = 0; l < k; ++l) v -= wave_sum(q[l] * v) * q[l];
+            for (int l = 0; l < k; ++l) v = fmaf(-wave_sum(q[l] * v), q[l], v);
             float n2 = wave_sum(v * v);
             if (k > 0 && n2 < 1e-4f * n0) {  // cancellation: project once more
 #pragma unroll
-                for (int l = 0; l < k; ++l) v -= wave_sum(q[l] * v) * q[l];
+                for (int l = 0; l < k; ++l) v = fmaf(-wave_sum(q[l] * v), q[l], v);
                 n2 = wave_sum(v * v);
             }
             if (n2 > 1e-30f) {
@@ -159,8 +165,9 @@ __device__ __forceinline__ void project_out(const Deflation &dfl, int lane, floa
     }
 }
 
-// z = B q for the four per-lane columns q (row `lane` of B in b).
-__device__ __forceinline__ void block_matvec(const float (&b)[kBeads], int lane,
+// z = B q for the four per-lane columns q (row `lane` of B in b, whose
+// diagonal entry is off by diag_err).
+__device__ __forceinline__ void block_matvec(const float (&b)[kBeads], float diag_err, int lane,
                                              const float (&q)[kBlk], float4 *s_q, float (&z)[kBlk]) {
     s_q[lane] = make_float4(q[0], q[1], q[2], q[3]);
     __syncthreads();
@@ -177,6 +184,8 @@ __device__ __forceinline__ void block_matvec(const float (&b)[kBeads], int lane,
         // LDS reads are hoisted and the register file overflows)
         if (j % 8 == 7) __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int k = 0; k < kBlk; ++k) z[k] = fmaf(-diag_err, q[k], z[k]);
     __syncthreads();
 }
 
@@ -206,15 +215,15 @@ __device__ __forceinline__ bool may_hide(const float (&d)[kBlk], float rho) {
 // never negative, and projecting directions out, which leaves 0 in their
 // place, cannot change the three largest.)  On return theta (descending) and
 // vec (lane = bead) hold the last Ritz pairs.
-__device__ __forceinline__ void subspace(const float (&b)[kBeads], Deflation &dfl, int32_t max_iters, int lane,
-                                         float4 *s_q, float (&theta)[kBlk], float (&vec)[kBlk]) {
+__device__ __forceinline__ void subspace(const float (&b)[kBeads], float diag_err, Deflation &dfl, int32_t max_iters,
+                                         int lane, float4 *s_q, float (&theta)[kBlk], float (&vec)[kBlk]) {
     float q[kBlk], z[kBlk];
 #pragma unroll
     for (int k = 0; k < kBlk; ++k) z[k] = start_vec(lane, k);
     int pass = 0, steps = 0;
     for (int it = 0;; ++it) {
         orthonormalise(lane, z, q);
-        block_matvec(b, lane, q, s_q, z);
+        block_matvec(b, diag_err, lane, q, s_q, z);
         project_out(dfl, lane, z);
         if (it == 0) continue;  // the first product only seeds the subspace
         float h[kBlk][kBlk], wl[kBlk];
@@ -222,7 +231,7 @@ __device__ __forceinline__ void subspace(const float (&b)[kBeads], Deflation &df
         for (int r = 0; r < kBlk; ++r)
 #pragma unroll
             for (int c = r; c < kBlk; ++c) {
-                const float sm = wave_sum(q[r] * z[c] + q[c] * z[r]) * 0.5f;
+                const float sm = wave_sum(fmaf(q[r], z[c], q[c] * z[r])) * 0.5f;
                 h[r][c] = sm;
                 h[c][r] = sm;
             }
@@ -251,8 +260,8 @@ __device__ __forceinline__ void subspace(const float (&b)[kBeads], Deflation &df
         float thmax = 0.f, rho = 3.4e38f;
 #pragma unroll
         for (int k = 0; k < kBlk; ++k) {
-            vec[k] = q[0] * w[0][k] + q[1] * w[1][k] + q[2] * w[2][k] + q[3] * w[3][k];
-            yv[k] = z[0] * w[0][k] + z[1] * w[1][k] + z[2] * w[2][k] + z[3] * w[3][k];
+            vec[k] = fmaf(q[3], w[3][k], fmaf(q[2], w[2][k], fmaf(q[1], w[1][k], q[0] * w[0][k])));
+            yv[k] = fmaf(z[3], w[3][k], fmaf(z[2], w[2][k], fmaf(z[1], w[1][k], z[0] * w[0][k])));
             theta[k] = d[k];
             thmax = fmaxf(thmax, fabsf(d[k]));
             rho = fminf(rho, fabsf(d[k]));
@@ -270,7 +279,7 @@ __device__ __forceinline__ void subspace(const float (&b)[kBeads], Deflation &df
 #pragma unroll
         for (int k = 0; k < kBlk; ++k) {
             if (!done || (!hide && k == 3)) break;  // wave-uniform
-            const float r = yv[k] - d[k] * vec[k];
+            const float r = fmaf(-d[k], vec[k], yv[k]);
             const float r2 = wave_sum(r * r);
             float tk = cap;
             if (!hide && d[k] > 0.f) {
@@ -322,7 +331,10 @@ __global__ __launch_bounds__(kLanes, 4) void k_mds(const float *__restrict__ map
     // row[j - 1] of lane i's contiguous packed row, and packed (j, i) for j < i,
     // i.e. col[c_j] with c_j = idx(j, j + 1) - j - 1; both are reads at a
     // per-lane base plus a constant offset, and a select keeps the valid one.
-    // Every read stays inside the 2016 entries.
+    // Every read stays inside the 2016 entries.  At j = i the loop squares a
+    // stand-in g (the entry before lane i's row) instead of the diagonal 0;
+    // g^2 is taken back out of the row sum here and out of every product B q
+    // (block_matvec's diag_err), which is cheaper than a select per entry.
     float b[kBeads];
     const float *row = xs + packed_index(i, i + 1) - i;
     const float *col = xs + i;
@@ -337,12 +349,16 @@ __global__ __launch_bounds__(kLanes, 4) void k_mds(const float *__restrict__ map
             const float dc = col[packed_index(j, j + 1) - j - 1];
             d = j < i ? dc : dr;
         }
-        b[j] = j == i ? 0.f : d * d;
+        b[j] = d * d;
         rsum += b[j];
     }
+    const float g = xs[i > 0 ? packed_index(i, i + 1) - 1 : 0];
+    const float g2 = g * g;
+    rsum -= g2;
     // B = -1/2 J A J: b_ij = -a_ij / 2 + u_i + u_j with u_i = mean_i / 2 - grand mean / 4.
     const float gmean = wave_sum(rsum) * (1.f / (kBeads * kBeads));
     const float u_i = 0.5f * (rsum * (1.f / kBeads)) - 0.25f * gmean;
+    const float diag_err = fmaf(g2, -0.5f, u_i + u_i) - (u_i + u_i);  // stored b_ii minus the true one
     s_mean[i] = u_i;
     __syncthreads();
     const float4 *s_u = reinterpret_cast<const float4 *>(s_mean);
@@ -357,7 +373,7 @@ __global__ __launch_bounds__(kLanes, 4) void k_mds(const float *__restrict__ map
 
     float theta[kBlk], vec[kBlk];
     Deflation dfl{reinterpret_cast<float *>(s_map), 0};  // the packed map is dead once B is in registers
-    subspace(b, dfl, max_iters, i, s_q, theta, vec);
+    subspace(b, diag_err, dfl, max_iters, i, s_q, theta, vec);
 
     // Sign each column by its largest-magnitude entry (lowest bead on ties).
     float out[3];
