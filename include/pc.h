@@ -229,8 +229,8 @@ PC_API pc_status pc_seam_mean_abs(const float *state, const pc_layout *layout, f
  *   max_iters cap on the Rayleigh-Ritz steps of a map over all passes, 1..256
  *             (0 selects 128).  Maps that are Euclidean up to rounding take 1-4;
  *             the cap is reached only by maps far from any point cloud.
- * Errors: NULL maps/coords; n_maps < 0 or overflowing; max_iters out of range.
- * n_maps = 0 is a no-op.
+ * Errors: NULL maps/coords (when n_maps > 0); n_maps < 0 or overflowing;
+ * max_iters out of range.  n_maps = 0 is a no-op and accepts NULL pointers.
  */
 PC_API pc_status pc_mds_recover(const float *maps, int64_t n_maps, float *coords, float *eigvals,
                          int32_t max_iters, void *stream);

@@ -134,6 +134,7 @@ def test_other_validation(lib):
     assert lib.pc_mds_recover(FAKE, -1, FAKE, None, 0, None) == -2
     assert lib.pc_mds_recover(FAKE, 10, FAKE, None, 999, None) == -4
     assert lib.pc_mds_recover(None, 10, FAKE, None, 0, None) == -1
+    assert lib.pc_mds_recover(None, 0, None, None, 0, None) == 0          # empty batch: a no-op
     assert lib.pc_mds_recover(ctypes.c_void_p(4104), 10, FAKE, None, 0, None) == -3
     assert lib.pc_init_state(None, ctypes.byref(lay), 0, None) == -1
     assert lib.pc_philox_fill(ctypes.c_void_p(4097), ctypes.byref(lay), 0, 0, None) == -3

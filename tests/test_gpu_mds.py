@@ -119,3 +119,12 @@ def test_hidden_third_eigenvalue_default_budget():
     coords, _ = gpu_mds(maps)
     oc = [mds.classical_mds(m.astype(np.float64))[0] for m in maps]
     assert dist_err(coords, oc) <= DIST_RTOL
+
+
+def test_empty_batch_is_a_no_op():
+    torch, dev = torch_dev()
+    say("mds on an empty batch")
+    maps = torch.empty(0, dtype=torch.float32, device=dev)
+    coords = torch.empty(0, dtype=torch.float32, device=dev)
+    pc.pc_mds_recover(maps, coords)
+    torch.cuda.synchronize()

@@ -316,11 +316,12 @@ pc_status pc_seam_mean_abs(const float *state, const pc_layout *layout, float *o
 
 pc_status pc_mds_recover(const float *maps, int64_t n_maps, float *coords, float *eigvals, int32_t max_iters,
                          void *stream) {
-    if (!maps || !coords) return fail(PC_ERR_NULL, "maps and coords are required");
     if (n_maps < 0 || n_maps > 0x7FFFFFFFLL) return fail(PC_ERR_SHAPE, "n_maps = %lld outside 0..2^31-1",
                                                          static_cast<long long>(n_maps));
     if (max_iters == 0) max_iters = 128;
     if (max_iters < 1 || max_iters > 256) return fail(PC_ERR_PARAM, "max_iters = %d outside 1..256", max_iters);
+    if (n_maps == 0) return ok();  // nothing to read or write; the pointers may be NULL
+    if (!maps || !coords) return fail(PC_ERR_NULL, "maps and coords are required");
     if (!aligned16(maps) || !aligned16(coords) || (eigvals && !aligned16(eigvals)))
         return fail(PC_ERR_ALIGN, "device arrays must be 16-byte aligned");
     return hip_status(pc::launch_mds(maps, n_maps, coords, eigvals, max_iters, static_cast<hipStream_t>(stream)),
