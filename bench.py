@@ -290,8 +290,8 @@ def cpu_model() -> str:
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: the workloads need no inter-GPU communication and this build runs "
-              "on a single MI355X; --gpus N > 1 is not supported.", file=sys.stderr)
+        print("bench.py measures one GPU: the workloads need no inter-GPU communication and the library "
+              "runs on a single MI355X; --gpus N > 1 is not supported.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -25,7 +25,7 @@ def declared():
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(_lib.LIB_PATH):
-        pytest.fail("libpc.so is not built (run __graft_entry__.build())")
+        pytest.fail("libpc.so is not built (python -m tiled_genome_diffusion_amd.build)")
     return _lib.load()
 
 
