@@ -2,18 +2,21 @@
 // owning bead i.
 //
 //   1. The packed map is staged in LDS (504 coalesced float4 loads); lane i
-//      gathers row i of A = D o D into 64 VGPRs.
+//      gathers row i of A = D o D into 64 VGPRs (two constant-offset LDS
+//      reads and a select per entry).
 //   2. Double centring B = J A J (times -1/2) from the row means (LDS) and the
 //      grand mean (wavefront reduction); row i of B stays in VGPRs.
 //   3. Block-4 subspace iteration with Rayleigh-Ritz: Q <- orth(Z) by
-//      modified Gram-Schmidt, Z = B Q (Q broadcast from LDS, 256 FMAs per
-//      lane), H = Q^T Z by DPP wavefront reductions, a 4x4 Jacobi eigensolve
-//      (wave-uniform), Ritz vectors V = Q W, Z W = B V and the residuals
-//      ||B V_k - theta_k V_k|| of the three largest.  Stops when each is
-//      small against its pair's gap (eigenvector error ~ residual / gap) or
-//      after max_iters Rayleigh-Ritz steps in all.  The workgroup is capped
-//      at 128 VGPRs so four maps run per SIMD (the kernel is VALU-bound; four
-//      waves beat three by 12% on MI355X).
+//      modified Gram-Schmidt (a column that cancels is projected twice),
+//      Z = B Q (Q broadcast from LDS, 256 FMAs per lane), H = Q^T Z by DPP
+//      wavefront reductions, a 4x4 Jacobi eigensolve (wave-uniform values,
+//      eigenvector rows spread over lanes 0..3), Ritz vectors V = Q W,
+//      Z W = B V and the residuals ||B V_k - theta_k V_k|| of the three
+//      largest.  Stops when each is small against its pair's gap
+//      (eigenvector error ~ residual / gap) or after max_iters Rayleigh-Ritz
+//      steps in all.  The workgroup is capped at 128 VGPRs so four maps run
+//      per SIMD (the kernel is VALU-bound; four waves beat three by 12% and
+//      five, which spill, by -14% on MI355X).
 //   4. The iteration finds the eigenvalues of largest magnitude.  If negative
 //      ones could hide a positive eigenvalue (the third largest Ritz value is
 //      below the smallest magnitude found), the negative Ritz vectors that
