@@ -128,3 +128,17 @@ def test_empty_batch_is_a_no_op():
     coords = torch.empty(0, dtype=torch.float32, device=dev)
     pc.pc_mds_recover(maps, coords)
     torch.cuda.synchronize()
+
+
+def test_noise_maps_stay_finite_and_ordered():
+    # maps with no geometry at all (what a sampler fed random noise predictions ends on):
+    # the iteration may hit its cap, but every output is finite, the eigenvalues come out in
+    # descending order, and two runs agree bitwise
+    say("mds on pure-noise maps")
+    rng = np.random.default_rng(9)
+    maps = np.abs(rng.standard_normal((256, 2016)) * 10).astype(np.float32)
+    coords, eig = gpu_mds(maps)
+    coords2, eig2 = gpu_mds(maps)
+    assert np.all(np.isfinite(coords)) and np.all(np.isfinite(eig))
+    assert np.all(eig[:, 0] >= eig[:, 1]) and np.all(eig[:, 1] >= eig[:, 2])
+    assert np.array_equal(coords, coords2) and np.array_equal(eig, eig2)

@@ -15,8 +15,8 @@
 //      largest.  Stops when each is small against its pair's gap
 //      (eigenvector error ~ residual / gap) or after max_iters Rayleigh-Ritz
 //      steps in all.  The workgroup is capped at 128 VGPRs so four maps run
-//      per SIMD (the kernel is VALU-bound; four waves beat three by 12% and
-//      five, which spill, by -14% on MI355X).
+//      per SIMD (the kernel is VALU-bound; on MI355X four waves beat three by
+//      12%, and five need 96 VGPRs, spill and run 14% slower).
 //   4. The iteration finds the eigenvalues of largest magnitude.  If negative
 //      ones could hide a positive eigenvalue (the third largest Ritz value is
 //      below the smallest magnitude found), the negative Ritz vectors that
