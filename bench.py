@@ -331,16 +331,19 @@ def main():
     def one_pass(events=None, sd=seeds[0]):
         if events:
             events[3].record(stream)
-        pc.pc_init_state(state, lay, sd)
-        if events:
-            events[0].record(stream)
         if args.eps_buffers:
+            pc.pc_init_state(state, lay, sd)
+            if events:
+                events[0].record(stream)
             for i in range(n_steps):
                 pc.pc_ddim_cfg_step_eps(state, eps_c, eps_u, list(wl.w), lay, a_t[i], a_n[i], wl.eta, sd,
                                         i + 1, project_seams=bool(project))
         else:
+            if events:
+                events[0].record(stream)
+            # x_T is drawn inside the first step (no fill, no read of the state)
             pc.pc_ddim_sample(state, refs[sd][0], refs[sd][1], list(wl.w), lay, n_steps, wl.eta, sd,
-                              project_every=project, init=False)
+                              project_every=project, init=True)
         if events:
             events[1].record(stream)
         pc.pc_mds_recover(state, coords)
@@ -351,7 +354,8 @@ def main():
         one_pass(sd=seeds[k % len(seeds)])
     torch.cuda.synchronize()
 
-    # events per pass: [0] after x_T, [1] after the step loop, [2] after MDS, [3] before x_T
+    # events per pass: [3] pass start, [0] step loop start (after the fill in the eps-buffer form;
+    # otherwise x_T is drawn by the first step), [1] after the step loop, [2] after MDS
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     if args.graph:
         # three graphs per pass (x_T, the step loop, MDS); the events go between the replays
@@ -367,22 +371,25 @@ def main():
                                             sd0, i + 1, project_seams=bool(project))
             else:
                 pc.pc_ddim_sample(state, refs[sd0][0], refs[sd0][1], list(wl.w), lay, n_steps, wl.eta, sd0,
-                                  project_every=project, init=False)
+                                  project_every=project, init=True)
 
         def seg_mds():
             pc.pc_mds_recover(state, coords)
 
         graphs = []
-        for seg in (seg_init, seg_steps, seg_mds):
+        for seg in ((seg_init,) if args.eps_buffers else ()) + (seg_steps, seg_mds):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 seg()
             graphs.append(g)
+        if not args.eps_buffers:
+            graphs.insert(0, None)   # x_T is drawn inside the step-loop graph
 
         def one_pass(events=None, sd=sd0):  # noqa: F811 - the graph-replay form of the pass
             if events:
                 events[3].record(stream)
-            graphs[0].replay()
+            if graphs[0] is not None:
+                graphs[0].replay()
             if events:
                 events[0].record(stream)
             graphs[1].replay()
@@ -426,9 +433,14 @@ def main():
     launch_ms = step_ms / n_steps
     if args.eps_buffers:
         bytes_per_launch = lay.n_maps * STEP_BYTES_PER_MAP * 2   # + both noise predictions read
+        loop_bytes = n_steps * bytes_per_launch
     else:
         bytes_per_launch = lay.n_maps * STEP_BYTES_PER_MAP + lay.n_regions * REF_BYTES_PER_REGION
-    achieved = bytes_per_launch / (launch_ms * 1e-3) / 1e9
+        if project:   # the seam-owning kernel reads x_T: a fill writes it first
+            loop_bytes = n_steps * bytes_per_launch + lay.n_maps * STEP_BYTES_PER_MAP // 2
+        else:         # the first step draws x_T instead of reading it: it only writes the state
+            loop_bytes = n_steps * bytes_per_launch - lay.n_maps * STEP_BYTES_PER_MAP // 2
+    achieved = loop_bytes / (step_ms * 1e-3) / 1e9
     traffic, traffic_kernel = measured_traffic(wl.name) if not args.eps_buffers else (None, None)
 
     out = {
@@ -448,7 +460,7 @@ def main():
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "traffic_unit": "bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-scaled)",
                      "traffic_kernel": traffic_kernel, "launch_us": launch_ms * 1e3,
-                     "bytes_per_launch": bytes_per_launch,
+                     "bytes_per_launch": bytes_per_launch, "step_loop_bytes": loop_bytes,
                      "copy_ceiling": copy_gbs, "frac_of_copy": achieved / copy_gbs},
         "value_by_seed": by_seed,
         "value_sd_over_seeds": float(np.std(list(by_seed.values()), ddof=1)) if len(by_seed) > 1 else None,

@@ -173,6 +173,11 @@ PC_API pc_status pc_ddim_cfg_step_eps(float *state, const float *eps_cond, const
  * project_every = K > 0, the seams are projected in the step kernel after
  * every K-th step (section 4.3.2: a synchronisation interval K); K = 0 never
  * projects.  Arguments as for pc_init_state and pc_ddim_cfg_step.
+ *   init      1: start from x_T = the normals pc_init_state would write; the
+ *             first step draws them in registers, so the state is not read
+ *             before it (its prior contents are ignored).  0: start from the
+ *             state as given.  The result is bitwise the same as
+ *             pc_init_state followed by the steps.
  * Errors: those of pc_ddim_schedule and pc_ddim_cfg_step; project_every < 0;
  * project_every > 0 without chains.  On an error no step has been enqueued
  * unless it is PC_ERR_HIP.

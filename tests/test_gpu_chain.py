@@ -150,3 +150,18 @@ def test_chain_edge_cases(L, O, K):
         got = state.view(lay.n_maps, 2016)[torch.as_tensor(idx, device=dev)].cpu().numpy()
         fin, _, _, _ = oracle_columns(wl, 3, refs[0], refs[1], cols, 50, set(), project_every=K, chain=chain)
         assert normwise_err(got, fin.reshape(-1, 2016)) <= STATE_RTOL
+
+
+def test_whole_loop_with_drawn_x_T_matches_step_loop():
+    # pc_ddim_sample draws x_T inside its first (seam-projecting) step: bitwise the same as
+    # pc_init_state followed by the step loop, without reading the state's prior contents
+    torch, dev = torch_dev()
+    wl = get("chr22_chain")
+    say("chr22_chain: whole loop with x_T drawn in the first step vs step loop")
+    refs = upload_refs(wl, 5)
+    _, state, _ = run_steps(wl, 5, 50, [0], set(), refs=refs)
+    lay = layout_of(wl)
+    s2 = torch.full_like(state, float("nan"))
+    pc.pc_ddim_sample(s2, refs[2], refs[3], list(wl.w), lay, 50, wl.eta, 5, project_every=1)
+    torch.cuda.synchronize()
+    assert torch.equal(state, s2)

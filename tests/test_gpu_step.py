@@ -61,7 +61,7 @@ def test_whole_loop_entry_point_matches_step_loop():
     refs = upload_refs(wl, 1)
     _, state, _ = run_steps(wl, 1, 50, [0], set(), refs=refs)
     lay = layout_of(wl)
-    s2 = torch.empty_like(state)
+    s2 = torch.full_like(state, float("nan"))   # with init, the prior contents are never read
     pc.pc_ddim_sample(s2, refs[2], refs[3], list(wl.w), lay, 50, wl.eta, 1)
     torch.cuda.synchronize()
     assert torch.equal(state, s2)

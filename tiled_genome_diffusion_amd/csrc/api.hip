@@ -166,7 +166,8 @@ namespace {
 // stand-in on the references, otherwise the per-map noise predictions.
 pc_status ddim_step(const char *name, float *state, const float *x0_cond, const float *x0_uncond, const float *eps_c,
                     const float *eps_u, const float *w, const pc_layout *layout, double abar_t, double abar_next,
-                    double eta, uint64_t seed, uint32_t slot, int32_t project_seams, float *pre_disc, void *stream) {
+                    double eta, uint64_t seed, uint32_t slot, int32_t project_seams, float *pre_disc, void *stream,
+                    bool init = false) {
     int64_t n = 0;
     pc_status st = check_layout(layout, &n);
     if (st != PC_OK) return st;
@@ -208,12 +209,18 @@ pc_status ddim_step(const char *name, float *state, const float *x0_cond, const 
     args.k0 = static_cast<uint32_t>(seed);
     args.k1 = static_cast<uint32_t>(seed >> 32);
     args.slot = slot;
+    args.init = init ? 1u : 0u;
     const bool noise = args.c.sigma != 0.0f;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    if (chains && (project_seams || pre_disc))
+    if (chains && (project_seams || pre_disc)) {
+        if (init) {  // the seam-owning kernel reads x_T: fill it first
+            const hipError_t e = pc::launch_fill(state, n, args.k0, args.k1, 0u, false, s);
+            if (e != hipSuccess) return hip_status(e, "x_T fill launch");
+        }
         return hip_status(pc::launch_step_chain(state, x0_cond, x0_uncond, eps_c, eps_u, args, chain_args(layout),
                                                 project_seams != 0, pre_disc, noise, s),
                           "chain step launch");
+    }
     return hip_status(pc::launch_step_indep(state, x0_cond, x0_uncond, eps_c, eps_u, args, noise, s), "step launch");
 }
 
@@ -264,11 +271,13 @@ pc_status pc_ddim_sample(float *state, const float *x0_cond, const float *x0_unc
             if (1.0 - an - sg * sg < -1e-12) st = fail(PC_ERR_PARAM, "eta = %g too large at step %d", eta, i);
         }
     }
-    if (st == PC_OK && init) st = pc_init_state(state, layout, seed, stream);
+    // With init, the first step draws x_T in registers (the same Philox slot 0
+    // normals pc_init_state writes) instead of reading a filled state.
     for (int i = 0; st == PC_OK && i < n_steps; ++i) {
         const int proj = project_every > 0 && (i + 1) % project_every == 0;
-        st = pc_ddim_cfg_step(state, x0_cond, x0_uncond, w, layout, sched[i], sched[n_steps + i], eta, seed,
-                              static_cast<uint32_t>(i + 1), proj, nullptr, stream);
+        st = ddim_step("pc_ddim_sample", state, x0_cond, x0_uncond, nullptr, nullptr, w, layout, sched[i],
+                       sched[n_steps + i], eta, seed, static_cast<uint32_t>(i + 1), proj, nullptr, stream,
+                       init && i == 0);
     }
     delete[] sched;
     return st;

@@ -164,6 +164,8 @@ struct StepArgs {
     int32_t maps_per_block;   // independent layout: maps of one (r, g) per workgroup
     int32_t blocks_per_rg;
     uint32_t k0, k1, slot;    // Philox key words and step slot
+    uint32_t init;            // 1: the state holds no x_T yet; draw it from slot 0 instead of reading it
+                              // (independent-map kernel only)
 };
 
 struct ChainArgs {

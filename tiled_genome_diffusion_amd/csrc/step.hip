@@ -101,9 +101,15 @@ __device__ __forceinline__ void step_maps(float *__restrict__ state, const float
                                           const float *__restrict__ eps_u, size_t map0, uint32_t t0, uint32_t q,
                                           float4 xc, float4 xu, float w, const StepArgs &a) {
     float4 x[U], ec[U], eu[U];
+    if (a.init) {  // first step of a run: x_T is drawn here, not read (wave-uniform)
+#pragma unroll
+        for (int u = 0; u < U; ++u) x[u] = philox_normals(q, t0 + u, 0u, a.k0, a.k1);
+    } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) x[u] = ld_state<NT>(state, (map0 + u) * kQuads + q);
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        x[u] = ld_state<NT>(state, (map0 + u) * kQuads + q);
         if (EPS) {
             ec[u] = ld_state<NT>(eps_c, (map0 + u) * kQuads + q);
             eu[u] = ld_state<NT>(eps_u, (map0 + u) * kQuads + q);
