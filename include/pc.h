@@ -28,8 +28,9 @@
  *         sqrt(-2 ln u1) cos(2 pi u2), then sqrt(-2 ln u1) sin(2 pi u2).
  * Memory: every array argument marked "device" is device memory owned by the
  *         caller and must be 16-byte aligned; "host" arrays are host memory.
- *         The library allocates and frees nothing and keeps no state between
- *         calls; it is safe to call from several threads.
+ *         The library allocates no device memory and keeps no state between
+ *         calls (pc_ddim_sample holds its schedule in a host buffer for the
+ *         length of the call); it is safe to call from several threads.
  * Stream: `stream` is a hipStream_t (NULL = the null stream).  Device work is
  *         enqueued asynchronously on it; nothing synchronises.
  * Errors: argument errors are detected before any launch and return a
