@@ -43,6 +43,8 @@ def parse():
                    help="base seeds the timed passes cycle through (inputs and noise); per-seed rates are reported")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target duration of the oracle baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-only", action="store_true",
+                   help="no GPU: print only the oracle baseline of the workload (one JSON line)")
     p.add_argument("--eps-buffers", action="store_true",
                    help="step with noise predictions read from buffers (the interface of a trained denoiser) "
                         "instead of the point-mass stand-in: 16 B per element-step instead of 8")
@@ -309,6 +311,10 @@ def main():
     if args.copy_only:
         return copy_only(args, wl)
     n_steps = args.n_steps or wl.n_steps[0]
+    if args.cpu_only:
+        print(json.dumps({"workload": wl.name, "ddim_steps": n_steps,
+                          "cpu_baseline": cpu_baseline(wl, n_steps, args.seed, args.cpu_seconds)}), flush=True)
+        return None
     if args.sync_ablation:
         return sync_ablation(args, wl, n_steps)
     dev = torch.device("cuda:0")
