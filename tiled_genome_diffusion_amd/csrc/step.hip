@@ -165,16 +165,19 @@ __global__ __launch_bounds__(kThreads) void k_step_indep(float *__restrict__ sta
 //     values (beads 64-O..63) go to LDS;
 //   * lanes of seam lines step tile k+1's quads instead (with tile k+1's
 //     noise and references) and put its left-seam values in LDS; tile k+1's
-//     workgroup skips those lines, and tile 0 steps them for itself too;
+//     workgroup skips those lines;
+//   * tile 0's seam lines, which no left neighbour covers, are stepped by the
+//     seam-line lanes of the chain's last tile, which have no right
+//     neighbour to cover (tile 0's left seam is not shared: plain stores);
 //   * after one barrier both sides form the float32 mean (left + right) * 0.5
 //     (with PROJECT; otherwise each copy keeps its stepped value) and store
 //     whole float4 quads.
-// Every quad is stepped once, every store is a full float4, and no cache line
-// is written by two workgroups.  Each lane runs one stepping task per map
-// (two only in tile 0's seam lines), so waves stay in lockstep.  With DISC an
-// otherwise idle lane per map sums the squared seam differences in pair order
-// and stores the RMS per (seam, g, s).  LDS is double-buffered by iteration
-// parity, so one barrier per iteration suffices.
+// Every quad is stepped once, every store is a full float4, no cache line is
+// written by two workgroups, and every lane runs exactly one stepping task
+// per map.  With DISC an otherwise idle lane per map sums the squared seam
+// differences in pair order and stores the RMS per (seam, g, s).  LDS is
+// double-buffered by iteration parity, so one barrier per iteration
+// suffices.
 template <int U, bool PROJECT, bool DISC, bool NOISE, bool NT, bool EPS>
 __global__ __launch_bounds__(kThreads) void k_step_chain(float *__restrict__ state, const float *__restrict__ x0c,
                                                          const float *__restrict__ x0u,
@@ -222,24 +225,19 @@ __global__ __launch_bounds__(kThreads) void k_step_chain(float *__restrict__ sta
     }
     const bool right_quad = rp[0] >= 0 || rp[1] >= 0 || rp[2] >= 0 || rp[3] >= 0;
     const bool left_quad = lp[0] >= 0 || lp[1] >= 0 || lp[2] >= 0 || lp[3] >= 0;
-    // task 0: tile k's quad, or tile k+1's for seam lines of tiles k > 0; task 1: tile 0's halo
-    const bool own = active && !(seam_line && k > 0);
-    const bool halo = seam_line && owns_seam;
-    const bool t0 = own || halo;
-    const bool t0_halo = !own && halo;
-    const bool t1 = own && halo;  // tile 0 only
+    // The lane's one task: tile k's quad (plain and right-seam lines), tile
+    // k+1's (seam lines, k < L-1) or tile 0's (seam lines of the last tile).
+    const bool own = active && !seam_line;
+    const bool halo = active && seam_line && owns_seam;
+    const int dt = own ? 0 : (owns_seam ? 1 : -(L - 1));  // tile offset of the task
+    const size_t off0 = static_cast<size_t>(static_cast<ptrdiff_t>(dt) * n_cols);  // map offset (wraps for dt < 0)
 
-    float4 rc0 = make_float4(0.f, 0.f, 0.f, 0.f), ru0 = rc0, rc1 = rc0, ru1 = rc0;
-    if (t0 && !EPS) {
-        const size_t rr = static_cast<size_t>(r + (t0_halo ? 1 : 0));
+    float4 rc0 = make_float4(0.f, 0.f, 0.f, 0.f), ru0 = rc0;
+    if (active && !EPS) {
+        const size_t rr = static_cast<size_t>(r + dt);
         rc0 = ld4(x0c, rr * kQuads + q);
         ru0 = ld4(x0u, rr * kQuads + q);
     }
-    if (t1 && !EPS) {
-        rc1 = ld4(x0c, static_cast<size_t>(r + 1) * kQuads + q);
-        ru1 = ld4(x0u, static_cast<size_t>(r + 1) * kQuads + q);
-    }
-    const size_t off0 = t0_halo ? static_cast<size_t>(n_cols) : 0;  // map offset of task 0
 
     const int s0 = chunk * a.maps_per_block;
     const int s1 = s0 + a.maps_per_block < a.S ? s0 + a.maps_per_block : a.S;
@@ -247,62 +245,42 @@ __global__ __launch_bounds__(kThreads) void k_step_chain(float *__restrict__ sta
     int par = 0;
     for (int sb = s0; sb < s1; sb += U, par ^= 1) {
         const int nu = s1 - sb < U ? s1 - sb : U;
-        float4 y0[U], y1[U];
+        float4 y0[U];
         {
-            float4 x0[U], x1[U], e0c[U], e0u[U], e1c[U], e1u[U];
+            float4 x0[U], e0c[U], e0u[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                if (u < nu) {
+                if (u < nu && active) {
                     const size_t m0 = (t_base + sb + u + off0) * kQuads + q;
-                    const size_t m1 = (t_base + sb + u + n_cols) * kQuads + q;
-                    if (t0) {
-                        x0[u] = ld_state<NT>(state, m0);
-                        if (EPS) {
-                            e0c[u] = ld_state<NT>(eps_c, m0);
-                            e0u[u] = ld_state<NT>(eps_u, m0);
-                        }
-                    }
-                    if (t1) {
-                        x1[u] = ld_state<NT>(state, m1);
-                        if (EPS) {
-                            e1c[u] = ld_state<NT>(eps_c, m1);
-                            e1u[u] = ld_state<NT>(eps_u, m1);
-                        }
+                    x0[u] = ld_state<NT>(state, m0);
+                    if (EPS) {
+                        e0c[u] = ld_state<NT>(eps_c, m0);
+                        e0u[u] = ld_state<NT>(eps_u, m0);
                     }
                 }
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 if (u >= nu) break;
-                const size_t map = t_base + sb + u;
-                if (t0) {
-                    const uint32_t m0 = static_cast<uint32_t>(map + off0);
-                    const float4 z = NOISE ? philox_normals(q, m0, a.slot, a.k0, a.k1)
-                                           : make_float4(0.f, 0.f, 0.f, 0.f);
-                    y0[u] = EPS ? step4<true>(x0[u], e0c[u], e0u[u], w, a.c, z)
-                                : step4<false>(x0[u], rc0, ru0, w, a.c, z);
-                }
-                if (t1) {
-                    const uint32_t m1 = static_cast<uint32_t>(map + n_cols);
-                    const float4 z = NOISE ? philox_normals(q, m1, a.slot, a.k0, a.k1)
-                                           : make_float4(0.f, 0.f, 0.f, 0.f);
-                    y1[u] = EPS ? step4<true>(x1[u], e1c[u], e1u[u], w, a.c, z)
-                                : step4<false>(x1[u], rc1, ru1, w, a.c, z);
-                }
-                // right-seam values of tile k (task 0 of own lanes)
+                if (!active) continue;
+                const uint32_t m0 = static_cast<uint32_t>(t_base + sb + u + off0);
+                const float4 z = NOISE ? philox_normals(q, m0, a.slot, a.k0, a.k1)
+                                       : make_float4(0.f, 0.f, 0.f, 0.f);
+                y0[u] = EPS ? step4<true>(x0[u], e0c[u], e0u[u], w, a.c, z)
+                            : step4<false>(x0[u], rc0, ru0, w, a.c, z);
+                // right-seam values of tile k (own lanes)
                 if (own && owns_seam && right_quad) {
                     if (rp[0] >= 0) s_right[par][u][rp[0]] = y0[u].x;
                     if (rp[1] >= 0) s_right[par][u][rp[1]] = y0[u].y;
                     if (rp[2] >= 0) s_right[par][u][rp[2]] = y0[u].z;
                     if (rp[3] >= 0) s_right[par][u][rp[3]] = y0[u].w;
                 }
-                // left-seam values of tile k+1 (task 0 of halo lanes, task 1 in tile 0)
+                // left-seam values of tile k+1 (halo lanes)
                 if (halo && left_quad) {
-                    const float4 h = t1 ? y1[u] : y0[u];
-                    if (lp[0] >= 0) s_left[par][u][lp[0]] = h.x;
-                    if (lp[1] >= 0) s_left[par][u][lp[1]] = h.y;
-                    if (lp[2] >= 0) s_left[par][u][lp[2]] = h.z;
-                    if (lp[3] >= 0) s_left[par][u][lp[3]] = h.w;
+                    if (lp[0] >= 0) s_left[par][u][lp[0]] = y0[u].x;
+                    if (lp[1] >= 0) s_left[par][u][lp[1]] = y0[u].y;
+                    if (lp[2] >= 0) s_left[par][u][lp[2]] = y0[u].z;
+                    if (lp[3] >= 0) s_left[par][u][lp[3]] = y0[u].w;
                 }
             }
         }
@@ -319,15 +297,13 @@ __global__ __launch_bounds__(kThreads) void k_step_chain(float *__restrict__ sta
                     if (rp[3] >= 0) y0[u].w = (y0[u].w + s_left[par][u][rp[3]]) * 0.5f;
                 }
                 if (halo && left_quad) {
-                    float4 &h = t1 ? y1[u] : y0[u];
-                    if (lp[0] >= 0) h.x = (s_right[par][u][lp[0]] + h.x) * 0.5f;
-                    if (lp[1] >= 0) h.y = (s_right[par][u][lp[1]] + h.y) * 0.5f;
-                    if (lp[2] >= 0) h.z = (s_right[par][u][lp[2]] + h.z) * 0.5f;
-                    if (lp[3] >= 0) h.w = (s_right[par][u][lp[3]] + h.w) * 0.5f;
+                    if (lp[0] >= 0) y0[u].x = (s_right[par][u][lp[0]] + y0[u].x) * 0.5f;
+                    if (lp[1] >= 0) y0[u].y = (s_right[par][u][lp[1]] + y0[u].y) * 0.5f;
+                    if (lp[2] >= 0) y0[u].z = (s_right[par][u][lp[2]] + y0[u].z) * 0.5f;
+                    if (lp[3] >= 0) y0[u].w = (s_right[par][u][lp[3]] + y0[u].w) * 0.5f;
                 }
             }
-            if (t0) st_state<NT>(state, (map + off0) * kQuads + q, y0[u]);
-            if (t1) st_state<NT>(state, (map + n_cols) * kQuads + q, y1[u]);
+            if (active) st_state<NT>(state, (map + off0) * kQuads + q, y0[u]);
             if (DISC && owns_seam && static_cast<int>(q) == kQuads + u) {  // an otherwise idle lane
                 float acc = 0.f;
                 for (int p = 0; p < NP; ++p) {
