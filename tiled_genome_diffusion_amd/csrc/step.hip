@@ -19,7 +19,7 @@ constexpr int kIndepMaps = 2;        // maps of one (region, weight) per workgro
 // and one map per workgroup streams fastest (measured on MI355X: 6.17 against
 // 5.95 TB/s for two maps).
 constexpr int kIndepUEps = 1, kIndepMapsEps = 1;
-constexpr int kChainU = 2;           // maps in flight per lane, chain layout
+constexpr int kChainU = 1;           // maps per lane per barrier, chain layout (measured best on MI355X)
 // Maps of one (tile, weight) per workgroup, chain layout: enough to amortise
 // the per-workgroup set-up and barriers, while keeping about kChainGrid
 // workgroups in the grid (measured best on MI355X: 8 for 16,384 maps, 16 for
