@@ -16,3 +16,11 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def repo_root():
     return ROOT
+
+
+def pytest_terminal_summary(terminalreporter):
+    gu = sys.modules.get("gpu_util")
+    if gu is not None and gu.WORST["checks"]:
+        terminalreporter.write_line(
+            f"largest normwise state error over {gu.WORST['checks']} GPU parity checks: "
+            f"{gu.WORST['state']:.3e} (bound 1e-5)")

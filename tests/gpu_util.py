@@ -41,12 +41,19 @@ def map_index(wl: Workload, r: int, g: int, s: int) -> int:
     return (r * wl.n_guidance + g) * wl.n_traj + s
 
 
+# Largest normwise state error seen by any parity check of the session (reported at the end).
+WORST = {"state": 0.0, "checks": 0}
+
+
 def normwise_err(gpu: np.ndarray, ref: np.ndarray) -> float:
     """Largest per-map max |gpu - ref| / max(1, max |ref|) over the leading axes."""
     g = np.asarray(gpu, dtype=np.float64).reshape(-1, PACKED)
     r = np.asarray(ref, dtype=np.float64).reshape(-1, PACKED)
     scale = np.maximum(1.0, np.abs(r).max(axis=1))
-    return float((np.abs(g - r).max(axis=1) / scale).max())
+    err = float((np.abs(g - r).max(axis=1) / scale).max())
+    WORST["state"] = max(WORST["state"], err)
+    WORST["checks"] += 1
+    return err
 
 
 def run_steps(wl: Workload, seed: int, n_steps: int, sample_idx, record, project: bool = True, pre_disc=False,
