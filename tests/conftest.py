@@ -24,3 +24,7 @@ def pytest_terminal_summary(terminalreporter):
         terminalreporter.write_line(
             f"largest normwise state error over {gu.WORST['checks']} GPU parity checks: "
             f"{gu.WORST['state']:.3e} (bound 1e-5)")
+    if gu is not None and gu.WORST["dist_checks"]:
+        terminalreporter.write_line(
+            f"largest relative MDS distance error over {gu.WORST['dist_checks']} maps: "
+            f"{gu.WORST['dist']:.3e} (bound 1e-4)")

@@ -42,7 +42,7 @@ def map_index(wl: Workload, r: int, g: int, s: int) -> int:
 
 
 # Largest normwise state error seen by any parity check of the session (reported at the end).
-WORST = {"state": 0.0, "checks": 0}
+WORST = {"state": 0.0, "checks": 0, "dist": 0.0, "dist_checks": 0}
 
 
 def normwise_err(gpu: np.ndarray, ref: np.ndarray) -> float:
@@ -53,6 +53,14 @@ def normwise_err(gpu: np.ndarray, ref: np.ndarray) -> float:
     err = float((np.abs(g - r).max(axis=1) / scale).max())
     WORST["state"] = max(WORST["state"], err)
     WORST["checks"] += 1
+    return err
+
+
+def rel_dist_err(dist_gpu: np.ndarray, dist_ref: np.ndarray) -> float:
+    """max |D_gpu - D_ref| / max D_ref for one map's pairwise distances."""
+    err = float(np.abs(np.asarray(dist_gpu) - np.asarray(dist_ref)).max() / np.asarray(dist_ref).max())
+    WORST["dist"] = max(WORST["dist"], err)
+    WORST["dist_checks"] += 1
     return err
 
 

@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 import tiled_genome_diffusion_amd as pc
-from gpu_util import DIST_RTOL, layout_of, run_steps, say, torch_dev, upload_refs
+from gpu_util import DIST_RTOL, layout_of, rel_dist_err, run_steps, say, torch_dev, upload_refs
 from oracle import layout, mds
 from workloads import get, packed_distances, pseudo_euclidean_map, random_walk, walk_rng
 
@@ -25,9 +25,7 @@ def dist_err(coords, maps_oracle_coords):
     """Per-map max |D_gpu - D_oracle| / max D_oracle, worst over maps."""
     worst = 0.0
     for c, o in zip(coords, maps_oracle_coords):
-        dg = mds.coords_distances(c)
-        do = mds.coords_distances(o)
-        worst = max(worst, float(np.abs(dg - do).max() / do.max()))
+        worst = max(worst, rel_dist_err(mds.coords_distances(c), mds.coords_distances(o)))
     return worst
 
 
@@ -58,8 +56,7 @@ def test_closed_form_shapes():
     assert eig[1, 0] == pytest.approx(64 * 3.5 ** 2 / 2, rel=1e-5)
     assert eig[1, 1] == pytest.approx(64 * 3.5 ** 2 / 2, rel=1e-5)
     for k, pts in ((0, line), (1, ring)):
-        d = mds.coords_distances(coords[k])
-        assert np.abs(d - packed_distances(pts)).max() <= DIST_RTOL * packed_distances(pts).max()
+        assert rel_dist_err(mds.coords_distances(coords[k]), packed_distances(pts)) <= DIST_RTOL
     assert np.all(coords[2] == 0.0) and np.all(eig[2] == 0.0)   # all-zero map
 
 

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import tiled_genome_diffusion_amd as pc
-from gpu_util import DIST_RTOL, STATE_RTOL, layout_of, normwise_err, say, torch_dev, upload_refs
+from gpu_util import DIST_RTOL, STATE_RTOL, layout_of, normwise_err, rel_dist_err, say, torch_dev, upload_refs
 from oracle import mds, sampler
 from workloads import Workload
 
@@ -79,5 +79,4 @@ def test_random_layout_matches_oracle(case):
     coords = coords.view(len(sample), 64, 3).cpu().numpy()
     for c, m in zip(coords, got[sample]):
         o, _ = mds.classical_mds(m.astype(np.float64))
-        dg, do = mds.coords_distances(c), mds.coords_distances(o)
-        assert np.abs(dg - do).max() <= DIST_RTOL * do.max()
+        assert rel_dist_err(mds.coords_distances(c), mds.coords_distances(o)) <= DIST_RTOL

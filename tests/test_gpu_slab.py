@@ -6,7 +6,8 @@ import numpy as np
 import pytest
 
 import tiled_genome_diffusion_amd as pc
-from gpu_util import DIST_RTOL, STATE_RTOL, layout_of, normwise_err, run_steps, say, torch_dev, upload_refs
+from gpu_util import (DIST_RTOL, STATE_RTOL, layout_of, normwise_err, rel_dist_err, run_steps, say, torch_dev,
+                      upload_refs)
 from oracle import mds, sampler
 from workloads import get
 
@@ -44,7 +45,6 @@ def test_genome_slab_sampled():
     got = coords.view(wl.n_maps, 64, 3)[torch.as_tensor(idx, device=dev)].cpu().numpy()
     for c, m in zip(got, rec[50]):
         o, _ = mds.classical_mds(m.astype(np.float64))
-        dg, do = mds.coords_distances(c), mds.coords_distances(o)
-        assert np.abs(dg - do).max() <= DIST_RTOL * do.max()
+        assert rel_dist_err(mds.coords_distances(c), mds.coords_distances(o)) <= DIST_RTOL
     del state, coords
     torch.cuda.empty_cache()
