@@ -469,7 +469,10 @@ def main():
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "traffic_unit": "bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-scaled)",
                      "traffic_kernel": traffic_kernel, "launch_us": launch_ms * 1e3,
-                     "bytes_per_launch": bytes_per_launch, "step_loop_bytes": loop_bytes,
+                     # achieved = bytes_per_launch / launch_us: both averaged over the loop's launches
+                     "bytes_per_launch": loop_bytes / n_steps, "step_loop_bytes": loop_bytes,
+                     # a launch that reads and writes the whole state: the basis of `traffic`
+                     "bytes_per_steady_launch": bytes_per_launch,
                      "copy_ceiling": copy_gbs, "frac_of_copy": achieved / copy_gbs},
         "value_by_seed": by_seed,
         "value_sd_over_seeds": float(np.std(list(by_seed.values()), ddof=1)) if len(by_seed) > 1 else None,
