@@ -445,10 +445,8 @@ def main():
         loop_bytes = n_steps * bytes_per_launch
     else:
         bytes_per_launch = lay.n_maps * STEP_BYTES_PER_MAP + lay.n_regions * REF_BYTES_PER_REGION
-        if project:   # the seam-owning kernel reads x_T: a fill writes it first
-            loop_bytes = n_steps * bytes_per_launch + lay.n_maps * STEP_BYTES_PER_MAP // 2
-        else:         # the first step draws x_T instead of reading it: it only writes the state
-            loop_bytes = n_steps * bytes_per_launch - lay.n_maps * STEP_BYTES_PER_MAP // 2
+        # the first step draws x_T instead of reading it: it only writes the state
+        loop_bytes = n_steps * bytes_per_launch - lay.n_maps * STEP_BYTES_PER_MAP // 2
     achieved = loop_bytes / (step_ms * 1e-3) / 1e9
     traffic, traffic_kernel = measured_traffic(wl.name) if not args.eps_buffers else (None, None)
 

@@ -213,12 +213,15 @@ pc_status ddim_step(const char *name, float *state, const float *x0_cond, const 
     const bool noise = args.c.sigma != 0.0f;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (chains && (project_seams || pre_disc)) {
-        if (init) {  // the seam-owning kernel reads x_T: fill it first
+        // x_T in the seam-owning kernel: drawn in registers where it has that
+        // form (projecting, no discrepancy output, references), else filled first
+        const bool draw = init && project_seams && !pre_disc && !eps;
+        if (init && !draw) {
             const hipError_t e = pc::launch_fill(state, n, args.k0, args.k1, 0u, false, s);
             if (e != hipSuccess) return hip_status(e, "x_T fill launch");
         }
         return hip_status(pc::launch_step_chain(state, x0_cond, x0_uncond, eps_c, eps_u, args, chain_args(layout),
-                                                project_seams != 0, pre_disc, noise, s),
+                                                project_seams != 0, pre_disc, noise, draw, s),
                           "chain step launch");
     }
     return hip_status(pc::launch_step_indep(state, x0_cond, x0_uncond, eps_c, eps_u, args, noise, s), "step launch");

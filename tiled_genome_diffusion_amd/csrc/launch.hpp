@@ -14,8 +14,10 @@ hipError_t launch_fill(void *out, int64_t n_maps, uint32_t k0, uint32_t k1, uint
 hipError_t launch_step_indep(float *state, const float *x0c, const float *x0u, const float *eps_c, const float *eps_u,
                              StepArgs a, bool noise, hipStream_t stream);
 
+// init: draw x_T in the step (only with project, no pre_disc and references).
 hipError_t launch_step_chain(float *state, const float *x0c, const float *x0u, const float *eps_c, const float *eps_u,
-                             StepArgs a, ChainArgs ch, bool project, float *pre_disc, bool noise, hipStream_t stream);
+                             StepArgs a, ChainArgs ch, bool project, float *pre_disc, bool noise, bool init,
+                             hipStream_t stream);
 
 hipError_t launch_seam_project(float *state, int32_t n_chains, int32_t n_cols, ChainArgs ch, hipStream_t stream);
 

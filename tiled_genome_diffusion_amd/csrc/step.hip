@@ -177,8 +177,9 @@ __global__ __launch_bounds__(kThreads) void k_step_indep(float *__restrict__ sta
 // per map.  With DISC an otherwise idle lane per map sums the squared seam
 // differences in pair order and stores the RMS per (seam, g, s).  LDS is
 // double-buffered by iteration parity, so one barrier per iteration
-// suffices.
-template <int U, bool PROJECT, bool DISC, bool NOISE, bool NT, bool EPS>
+// suffices.  INIT (the projecting first step of a run) draws x_T in
+// registers instead of reading a filled state.
+template <int U, bool PROJECT, bool DISC, bool NOISE, bool NT, bool EPS, bool INIT = false>
 __global__ __launch_bounds__(kThreads) void k_step_chain(float *__restrict__ state, const float *__restrict__ x0c,
                                                          const float *__restrict__ x0u,
                                                          const float *__restrict__ eps_c,
@@ -252,7 +253,9 @@ __global__ __launch_bounds__(kThreads) void k_step_chain(float *__restrict__ sta
             for (int u = 0; u < U; ++u) {
                 if (u < nu && active) {
                     const size_t m0 = (t_base + sb + u + off0) * kQuads + q;
-                    x0[u] = ld_state<NT>(state, m0);
+                    // INIT: first step of a run, x_T drawn here (Philox slot 0) instead of read
+                    x0[u] = INIT ? philox_normals(q, static_cast<uint32_t>(t_base + sb + u + off0), 0u, a.k0, a.k1)
+                                 : ld_state<NT>(state, m0);
                     if (EPS) {
                         e0c[u] = ld_state<NT>(eps_c, m0);
                         e0u[u] = ld_state<NT>(eps_u, m0);
@@ -361,7 +364,8 @@ hipError_t launch_step_indep(float *state, const float *x0c, const float *x0u, c
 }
 
 hipError_t launch_step_chain(float *state, const float *x0c, const float *x0u, const float *eps_c, const float *eps_u,
-                             StepArgs a, ChainArgs ch, bool project, float *pre_disc, bool noise, hipStream_t stream) {
+                             StepArgs a, ChainArgs ch, bool project, float *pre_disc, bool noise, bool init,
+                             hipStream_t stream) {
     const int64_t n_maps = static_cast<int64_t>(a.R) * a.G * a.S;
     int64_t mpb = (n_maps / kChainGrid) & ~int64_t(1);
     mpb = mpb < kChainMapsMin ? kChainMapsMin : (mpb > kChainMapsMax ? kChainMapsMax : mpb);
@@ -379,7 +383,17 @@ hipError_t launch_step_chain(float *state, const float *x0c, const float *x0u, c
     if (eps) PC_CHAIN(P, D, N, T, true); else PC_CHAIN(P, D, N, T, false)
 #define PC_CHAIN_NT(P, D, N) \
     if (nt) PC_CHAIN_E(P, D, N, true); else PC_CHAIN_E(P, D, N, false)
-    if (project) {
+    if (init) {  // the whole-loop entry point's first step: projecting, no discrepancy, references
+#define PC_CHAIN_INIT(N, T)                                                                                    \
+    hipLaunchKernelGGL((k_step_chain<kChainU, true, false, N, T, false, true>), grid, dim3(kThreads), 0, stream, \
+                       state, x0c, x0u, eps_c, eps_u, a, ch, pre_disc)
+        if (noise) {
+            if (nt) PC_CHAIN_INIT(true, true); else PC_CHAIN_INIT(true, false);
+        } else {
+            if (nt) PC_CHAIN_INIT(false, true); else PC_CHAIN_INIT(false, false);
+        }
+#undef PC_CHAIN_INIT
+    } else if (project) {
         if (disc) {
             if (noise) PC_CHAIN_NT(true, true, true); else PC_CHAIN_NT(true, true, false);
         } else {
