@@ -80,7 +80,8 @@ def measured_traffic(workload: str):
     return None, None
 
 
-STEP_SOURCES = ["tiled_genome_diffusion_amd/csrc/step.hip", "tiled_genome_diffusion_amd/csrc/common.hpp"]
+STEP_SOURCES = ["tiled_genome_diffusion_amd/csrc/step.hip", "tiled_genome_diffusion_amd/csrc/stream.hpp",
+                "tiled_genome_diffusion_amd/csrc/common.hpp"]
 
 
 def traffic_summary(args, wl):

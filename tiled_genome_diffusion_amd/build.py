@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpc.so")
-SOURCES = ["api.hip", "step.hip", "seam.hip", "mds.hip", "stitch.hip"]
+SOURCES = ["api.hip", "step.hip", "chain.hip", "seam.hip", "mds.hip", "stitch.hip"]
 ARCH = "gfx950"
 
 

@@ -1,77 +1,16 @@
-// Guided DDIM step kernels and the Philox fills.
-//
-// Thread mapping: a workgroup has 512 lanes; lane q < 504 owns float4 quad q
-// (packed elements 4q .. 4q+3) of every map the workgroup visits, so a
-// wavefront streams 1 KB of contiguous state per map.  Because q is fixed
-// per lane, the lane's reference values and the q-dependent part of its
-// Philox counter stay in registers across maps.  Lanes 504..511 only take
-// part in barriers.
-#include "common.hpp"
+// Guided DDIM step over independent maps, and the Philox fills.
 #include "launch.hpp"
+#include "stream.hpp"
 
 namespace pc {
 namespace {
 
-constexpr int kThreads = 512;
 constexpr int kIndepU = 2;           // maps in flight per lane, independent layout
 constexpr int kIndepMaps = 2;        // maps of one (region, weight) per workgroup
 // With noise predictions from buffers there are no references to amortise,
 // and one map per workgroup streams fastest (measured on MI355X: 6.17 against
 // 5.95 TB/s for two maps).
 constexpr int kIndepUEps = 1, kIndepMapsEps = 1;
-constexpr int kChainU = 1;           // maps per lane per barrier, chain layout (measured best on MI355X)
-// Maps of one (tile, weight) per workgroup, chain layout: enough to amortise
-// the per-workgroup set-up and barriers, while keeping about kChainGrid
-// workgroups in the grid (measured best on MI355X: 8 for 16,384 maps, 16 for
-// 32,000).
-constexpr int kChainMapsMin = 4, kChainMapsMax = 16, kChainGrid = 2048;
-// States well beyond the 256 MB Infinity Cache are streamed with
-// non-temporal loads and stores: each value is touched once per step, so
-// caching it only evicts the references.  Smaller states stay cacheable, so
-// consecutive steps can hit in the Infinity Cache (measured: a 258 MB chain
-// state steps 8% faster cached than streamed).
-constexpr size_t kStreamBytes = size_t(512) << 20;
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float4 ld4(const float *p, size_t quad) {
-    return reinterpret_cast<const float4 *>(p)[quad];
-}
-__device__ __forceinline__ void st4(float *p, size_t quad, float4 v) {
-    reinterpret_cast<float4 *>(p)[quad] = v;
-}
-template <bool NT>
-__device__ __forceinline__ float4 ld_state(const float *p, size_t quad) {
-    if (!NT) return ld4(p, quad);
-    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p) + quad);
-    return make_float4(v.x, v.y, v.z, v.w);
-}
-template <bool NT>
-__device__ __forceinline__ void st_state(float *p, size_t quad, float4 v) {
-    if (!NT) return st4(p, quad, v);
-    const f32x4 w = {v.x, v.y, v.z, v.w};
-    __builtin_nontemporal_store(w, reinterpret_cast<f32x4 *>(p) + quad);
-}
-
-// Step four elements.  EPS: (dc, du) are the network's conditional and
-// unconditional noise predictions; otherwise they are the reference maps of
-// the point-mass stand-in.
-template <bool EPS>
-__device__ __forceinline__ float4 step4(float4 x, float4 dc, float4 du, float w, const StepCoef &c, float4 z) {
-    float4 y;
-    if (EPS) {
-        y.x = ddim_guided_update(x.x, dc.x, du.x, w, c, z.x);
-        y.y = ddim_guided_update(x.y, dc.y, du.y, w, c, z.y);
-        y.z = ddim_guided_update(x.z, dc.z, du.z, w, c, z.z);
-        y.w = ddim_guided_update(x.w, dc.w, du.w, w, c, z.w);
-    } else {
-        y.x = ddim_cfg_element(x.x, dc.x, du.x, w, c, z.x);
-        y.y = ddim_cfg_element(x.y, dc.y, du.y, w, c, z.y);
-        y.z = ddim_cfg_element(x.z, dc.z, du.z, w, c, z.z);
-        y.w = ddim_cfg_element(x.w, dc.w, du.w, w, c, z.w);
-    }
-    return y;
-}
 
 // ---------------------------------------------------------------------------
 // Fills: raw Philox words or normals of one slot for maps [m0, m1) of a
@@ -154,172 +93,6 @@ __global__ __launch_bounds__(kThreads) void k_step_indep(float *__restrict__ sta
     for (; s < s1; ++s) step_maps<1, NOISE, NT, EPS>(state, eps_c, eps_u, t_base + s, t_base + s, q, xc, xu, w, a);
 }
 
-// ---------------------------------------------------------------------------
-// Chains.  Workgroups are laid out as for independent maps: one workgroup
-// steps a.maps_per_block maps of one tile k (region r = c L + k) and weight g.
-// Ownership is by 128-byte line (8 quads; a map is 63 lines): a line is a
-// "seam line" if it holds any element of the left seam (pairs of beads
-// 0..O-1).  Seam k, shared by tiles k and k+1, is resolved entirely by tile
-// k's workgroup:
-//   * lanes of plain and right-seam lines step tile k's quads; right-seam
-//     values (beads 64-O..63) go to LDS;
-//   * lanes of seam lines step tile k+1's quads instead (with tile k+1's
-//     noise and references) and put its left-seam values in LDS; tile k+1's
-//     workgroup skips those lines;
-//   * tile 0's seam lines, which no left neighbour covers, are stepped by the
-//     seam-line lanes of the chain's last tile, which have no right
-//     neighbour to cover (tile 0's left seam is not shared: plain stores);
-//   * after one barrier both sides form the float32 mean (left + right) * 0.5
-//     (with PROJECT; otherwise each copy keeps its stepped value) and store
-//     whole float4 quads.
-// Every quad is stepped once, every store is a full float4, no cache line is
-// written by two workgroups, and every lane runs exactly one stepping task
-// per map.  With DISC an otherwise idle lane per map sums the squared seam
-// differences in pair order and stores the RMS per (seam, g, s).  LDS is
-// double-buffered by iteration parity, so one barrier per iteration
-// suffices.  INIT (the projecting first step of a run) draws x_T in
-// registers instead of reading a filled state.
-template <int U, bool PROJECT, bool DISC, bool NOISE, bool NT, bool EPS, bool INIT = false>
-__global__ __launch_bounds__(kThreads) void k_step_chain(float *__restrict__ state, const float *__restrict__ x0c,
-                                                         const float *__restrict__ x0u,
-                                                         const float *__restrict__ eps_c,
-                                                         const float *__restrict__ eps_u, StepArgs a, ChainArgs ch,
-                                                         float *__restrict__ pre_disc) {
-    static_assert(U <= kThreads - kQuads, "the discrepancy of map u is summed by idle lane kQuads + u");
-    __shared__ float s_right[2][U][kMaxPairs];  // tile k's stepped right-seam values
-    __shared__ float s_left[2][U][kMaxPairs];   // tile k+1's stepped left-seam values
-
-    const uint32_t q = threadIdx.x;
-    const bool active = q < kQuads;
-    const uint32_t b = xcd_remap(blockIdx.x, gridDim.x);
-    const int rg = static_cast<int>(b) / a.blocks_per_rg;
-    const int chunk = static_cast<int>(b) - rg * a.blocks_per_rg;
-    const int r = rg / a.G;
-    const int g = rg - r * a.G;
-    const float w = a.w[g];
-    const int L = ch.chain_len, O = ch.overlap, NP = ch.n_pairs;
-    const int c = r / L;
-    const int k = r - c * L;
-    const int n_cols = a.G * a.S;
-    const bool owns_seam = k < L - 1;
-    const int off = kBeads - O;
-
-    // Seam membership of this lane's four elements (pair index or -1), and
-    // whether its 128-byte line (elements 32 m .. 32 m + 31) holds a
-    // left-seam element.  A line spans at most two rows of the map.
-    int lp[4], rp[4];
-#pragma unroll
-    for (int l = 0; l < 4; ++l) {
-        int i = 0, j = 1;
-        if (active) packed_row_col(static_cast<int>(4 * q) + l, i, j);
-        lp[l] = (active && j < O) ? block_pair_index(i, j, O) : -1;
-        rp[l] = (active && i >= off) ? block_pair_index(i - off, j - off, O) : -1;
-    }
-    bool seam_line = false;
-    if (active) {
-        const int e0 = static_cast<int>(q / 8) * 32, e1 = e0 + 31;
-        int i0, j0, i1, j1;
-        packed_row_col(e0, i0, j0);
-        packed_row_col(e1, i1, j1);
-        // row i0 from column j0 on, row i1 up to column j1: left-seam columns are < O
-        seam_line = (i0 <= O - 2 && j0 < O) || (i1 <= O - 2 && i1 > i0);
-    }
-    const bool right_quad = rp[0] >= 0 || rp[1] >= 0 || rp[2] >= 0 || rp[3] >= 0;
-    const bool left_quad = lp[0] >= 0 || lp[1] >= 0 || lp[2] >= 0 || lp[3] >= 0;
-    // The lane's one task: tile k's quad (plain and right-seam lines), tile
-    // k+1's (seam lines, k < L-1) or tile 0's (seam lines of the last tile).
-    const bool own = active && !seam_line;
-    const bool halo = active && seam_line && owns_seam;
-    const int dt = own ? 0 : (owns_seam ? 1 : -(L - 1));  // tile offset of the task
-    const size_t off0 = static_cast<size_t>(static_cast<ptrdiff_t>(dt) * n_cols);  // map offset (wraps for dt < 0)
-
-    float4 rc0 = make_float4(0.f, 0.f, 0.f, 0.f), ru0 = rc0;
-    if (active && !EPS) {
-        const size_t rr = static_cast<size_t>(r + dt);
-        rc0 = ld4(x0c, rr * kQuads + q);
-        ru0 = ld4(x0u, rr * kQuads + q);
-    }
-
-    const int s0 = chunk * a.maps_per_block;
-    const int s1 = s0 + a.maps_per_block < a.S ? s0 + a.maps_per_block : a.S;
-    const size_t t_base = static_cast<size_t>(rg) * a.S;
-    int par = 0;
-    for (int sb = s0; sb < s1; sb += U, par ^= 1) {
-        const int nu = s1 - sb < U ? s1 - sb : U;
-        float4 y0[U];
-        {
-            float4 x0[U], e0c[U], e0u[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                if (u < nu && active) {
-                    const size_t m0 = (t_base + sb + u + off0) * kQuads + q;
-                    // INIT: first step of a run, x_T drawn here (Philox slot 0) instead of read
-                    x0[u] = INIT ? philox_normals(q, static_cast<uint32_t>(t_base + sb + u + off0), 0u, a.k0, a.k1)
-                                 : ld_state<NT>(state, m0);
-                    if (EPS) {
-                        e0c[u] = ld_state<NT>(eps_c, m0);
-                        e0u[u] = ld_state<NT>(eps_u, m0);
-                    }
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                if (u >= nu) break;
-                if (!active) continue;
-                const uint32_t m0 = static_cast<uint32_t>(t_base + sb + u + off0);
-                const float4 z = NOISE ? philox_normals(q, m0, a.slot, a.k0, a.k1)
-                                       : make_float4(0.f, 0.f, 0.f, 0.f);
-                y0[u] = EPS ? step4<true>(x0[u], e0c[u], e0u[u], w, a.c, z)
-                            : step4<false>(x0[u], rc0, ru0, w, a.c, z);
-                // right-seam values of tile k (own lanes)
-                if (own && owns_seam && right_quad) {
-                    if (rp[0] >= 0) s_right[par][u][rp[0]] = y0[u].x;
-                    if (rp[1] >= 0) s_right[par][u][rp[1]] = y0[u].y;
-                    if (rp[2] >= 0) s_right[par][u][rp[2]] = y0[u].z;
-                    if (rp[3] >= 0) s_right[par][u][rp[3]] = y0[u].w;
-                }
-                // left-seam values of tile k+1 (halo lanes)
-                if (halo && left_quad) {
-                    if (lp[0] >= 0) s_left[par][u][lp[0]] = y0[u].x;
-                    if (lp[1] >= 0) s_left[par][u][lp[1]] = y0[u].y;
-                    if (lp[2] >= 0) s_left[par][u][lp[2]] = y0[u].z;
-                    if (lp[3] >= 0) s_left[par][u][lp[3]] = y0[u].w;
-                }
-            }
-        }
-        if (owns_seam) __syncthreads();
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (u >= nu) break;
-            const size_t map = t_base + sb + u;
-            if (PROJECT && owns_seam) {
-                if (own && right_quad) {  // left copy (tile k) + right copy (tile k+1)
-                    if (rp[0] >= 0) y0[u].x = (y0[u].x + s_left[par][u][rp[0]]) * 0.5f;
-                    if (rp[1] >= 0) y0[u].y = (y0[u].y + s_left[par][u][rp[1]]) * 0.5f;
-                    if (rp[2] >= 0) y0[u].z = (y0[u].z + s_left[par][u][rp[2]]) * 0.5f;
-                    if (rp[3] >= 0) y0[u].w = (y0[u].w + s_left[par][u][rp[3]]) * 0.5f;
-                }
-                if (halo && left_quad) {
-                    if (lp[0] >= 0) y0[u].x = (s_right[par][u][lp[0]] + y0[u].x) * 0.5f;
-                    if (lp[1] >= 0) y0[u].y = (s_right[par][u][lp[1]] + y0[u].y) * 0.5f;
-                    if (lp[2] >= 0) y0[u].z = (s_right[par][u][lp[2]] + y0[u].z) * 0.5f;
-                    if (lp[3] >= 0) y0[u].w = (s_right[par][u][lp[3]] + y0[u].w) * 0.5f;
-                }
-            }
-            if (active) st_state<NT>(state, (map + off0) * kQuads + q, y0[u]);
-            if (DISC && owns_seam && static_cast<int>(q) == kQuads + u) {  // an otherwise idle lane
-                float acc = 0.f;
-                for (int p = 0; p < NP; ++p) {
-                    const float d = s_right[par][u][p] - s_left[par][u][p];
-                    acc = fmaf(d, d, acc);
-                }
-                pre_disc[(static_cast<size_t>(c) * (L - 1) + k) * n_cols + static_cast<size_t>(g) * a.S + sb + u] =
-                    sqrtf(acc / static_cast<float>(NP));
-            }
-        }
-    }
-}
-
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -360,51 +133,6 @@ hipError_t launch_step_indep(float *state, const float *x0c, const float *x0u, c
     }
 #undef PC_INDEP_E
 #undef PC_INDEP
-    return hipGetLastError();
-}
-
-hipError_t launch_step_chain(float *state, const float *x0c, const float *x0u, const float *eps_c, const float *eps_u,
-                             StepArgs a, ChainArgs ch, bool project, float *pre_disc, bool noise, bool init,
-                             hipStream_t stream) {
-    const int64_t n_maps = static_cast<int64_t>(a.R) * a.G * a.S;
-    int64_t mpb = (n_maps / kChainGrid) & ~int64_t(1);
-    mpb = mpb < kChainMapsMin ? kChainMapsMin : (mpb > kChainMapsMax ? kChainMapsMax : mpb);
-    a.maps_per_block = static_cast<int32_t>(mpb);
-    a.blocks_per_rg = (a.S + a.maps_per_block - 1) / a.maps_per_block;
-    const int64_t blocks = static_cast<int64_t>(a.R) * a.G * a.blocks_per_rg;
-    const dim3 grid(static_cast<uint32_t>(blocks));
-    const bool disc = pre_disc != nullptr;
-    const bool nt = static_cast<size_t>(n_maps) * kPacked * 4 > kStreamBytes;
-    const bool eps = eps_c != nullptr;
-#define PC_CHAIN(P, D, N, T, E)                                                                                 \
-    hipLaunchKernelGGL((k_step_chain<kChainU, P, D, N, T, E>), grid, dim3(kThreads), 0, stream, state, x0c, x0u, \
-                       eps_c, eps_u, a, ch, pre_disc)
-#define PC_CHAIN_E(P, D, N, T) \
-    if (eps) PC_CHAIN(P, D, N, T, true); else PC_CHAIN(P, D, N, T, false)
-#define PC_CHAIN_NT(P, D, N) \
-    if (nt) PC_CHAIN_E(P, D, N, true); else PC_CHAIN_E(P, D, N, false)
-    if (init) {  // the whole-loop entry point's first step: projecting, no discrepancy, references
-#define PC_CHAIN_INIT(N, T)                                                                                    \
-    hipLaunchKernelGGL((k_step_chain<kChainU, true, false, N, T, false, true>), grid, dim3(kThreads), 0, stream, \
-                       state, x0c, x0u, eps_c, eps_u, a, ch, pre_disc)
-        if (noise) {
-            if (nt) PC_CHAIN_INIT(true, true); else PC_CHAIN_INIT(true, false);
-        } else {
-            if (nt) PC_CHAIN_INIT(false, true); else PC_CHAIN_INIT(false, false);
-        }
-#undef PC_CHAIN_INIT
-    } else if (project) {
-        if (disc) {
-            if (noise) PC_CHAIN_NT(true, true, true); else PC_CHAIN_NT(true, true, false);
-        } else {
-            if (noise) PC_CHAIN_NT(true, false, true); else PC_CHAIN_NT(true, false, false);
-        }
-    } else {
-        if (noise) PC_CHAIN_NT(false, true, true); else PC_CHAIN_NT(false, true, false);
-    }
-#undef PC_CHAIN_NT
-#undef PC_CHAIN_E
-#undef PC_CHAIN
     return hipGetLastError();
 }
 
