@@ -255,7 +255,10 @@ PC_API pc_status pc_mds_recover(const float *maps, int64_t n_maps, float *coords
  *   residual  device float [n_chains*(chain_len-1)][G][S], written: RMS
  *             distance over the shared beads after aligning seam k.
  * Shared beads must not be coplanar (the alignment is then not unique).
- * Errors: NULL pointers; bad layout; chain_len < 2.
+ * The seams are fitted independently in their tiles' own frames and the fits
+ * composed along the chain, which equals fitting each tile onto the already
+ * aligned one (a rigid motion of the target moves the best fit with it).
+ * Errors: NULL pointers; bad layout; chain_len outside 2..1024.
  */
 PC_API pc_status pc_kabsch_stitch(const float *coords, const pc_layout *layout, float *chain, float *residual,
                                   void *stream);

@@ -137,6 +137,9 @@ def test_other_validation(lib):
     assert lib.pc_mds_recover(None, 0, None, None, 0, None) == 0          # empty batch: a no-op
     assert lib.pc_mds_recover(ctypes.c_void_p(4104), 10, FAKE, None, 0, None) == -3
     assert lib.pc_init_state(None, ctypes.byref(lay), 0, None) == -1
+    assert lib.pc_kabsch_stitch(FAKE, ctypes.byref(lay), FAKE, FAKE, None) == -2            # no chains
+    long_chain = _lay(R=2048, G=1, S=1, L=2048, O=12)
+    assert lib.pc_kabsch_stitch(FAKE, ctypes.byref(long_chain), FAKE, FAKE, None) == -2     # chain_len > 1024
     assert lib.pc_philox_fill(ctypes.c_void_p(4097), ctypes.byref(lay), 0, 0, None) == -3
     assert lib.pc_ddim_sample(FAKE, FAKE, FAKE, W, ctypes.byref(lay), 7, 1000, 1e-4, 0.02, 1.0, 0, 0, 1, None) == -4
     assert lib.pc_ddim_sample(FAKE, FAKE, FAKE, W, ctypes.byref(lay), 50, 1000, 1e-4, 0.02, 1.0, 0, 1, 1, None) == -4

@@ -346,7 +346,8 @@ pc_status pc_kabsch_stitch(const float *coords, const pc_layout *layout, float *
     int64_t n = 0;
     const pc_status st = check_layout(layout, &n);
     if (st != PC_OK) return st;
-    if (layout->chain_len < 2) return fail(PC_ERR_SHAPE, "stitching needs chain_len >= 2");
+    if (layout->chain_len < 2 || layout->chain_len > 1024)
+        return fail(PC_ERR_SHAPE, "stitching needs 2 <= chain_len <= 1024 (got %d)", layout->chain_len);
     if (!aligned16(coords) || !aligned16(chain) || !aligned16(residual))
         return fail(PC_ERR_ALIGN, "device arrays must be 16-byte aligned");
     return hip_status(pc::launch_stitch(coords, layout->n_regions / layout->chain_len, layout->n_guidance,
