@@ -58,39 +58,67 @@ __global__ __launch_bounds__(256) void k_seam_disc(const float *__restrict__ sta
     rms[sc] = sqrtf(acc / static_cast<float>(NP));
 }
 
-// Paper-form seam discrepancy: one workgroup per (chain, seam, weight g);
-// lane p < NP sums pair p's left and right copies over the S trajectories in
-// index order (float64), and the mean over pairs of |mean left - mean right|
-// is a fixed-order tree over the lanes.
-__global__ __launch_bounds__(512) void k_seam_mean_abs(const float *__restrict__ state, int32_t G, int32_t S,
-                                                       ChainArgs ch, float *__restrict__ out) {
-    __shared__ double s_acc[512];
+// Paper-form seam discrepancy: one 1024-lane workgroup per (chain, seam,
+// weight g).  Lane (j, p), j < J = 1024 / NP, sums pair p's left and right
+// copies over the trajectories s = j, j + J, ... in index order (float64);
+// lane p then adds its J partial sums in order, and a fixed-order tree over
+// the pairs forms the mean of |mean left - mean right|.
+constexpr int kMeanAbsThreads = 1024;
+
+__global__ __launch_bounds__(kMeanAbsThreads) void k_seam_mean_abs(const float *__restrict__ state, int32_t G,
+                                                                  int32_t S, ChainArgs ch, float *__restrict__ out) {
+    __shared__ double s_l[kMeanAbsThreads], s_r[kMeanAbsThreads];
     const int NP = ch.n_pairs, L = ch.chain_len;
-    const int cj = static_cast<int>(blockIdx.x) / G;   // c (L - 1) + j
+    const int J = kMeanAbsThreads / NP;
+    const int cj = static_cast<int>(blockIdx.x) / G;   // c (L - 1) + seam
     const int g = static_cast<int>(blockIdx.x) - cj * G;
     const int c = cj / (L - 1);
-    const int j = cj - c * (L - 1);
+    const int seam = cj - c * (L - 1);
     const int n_cols = G * S;
-    double v = 0.0;
-    for (int p = threadIdx.x; p < NP; p += 512) {
+    const int t = static_cast<int>(threadIdx.x);
+    const int j = t / NP, p = t - j * NP;
+    double sl = 0.0, sr = 0.0;
+    if (j < J) {
         int li, ri;
         pair_indices(p, ch.overlap, li, ri);
-        const float *xl = state + (static_cast<size_t>(c * L + j) * n_cols + static_cast<size_t>(g) * S) * kPacked + li;
+        const float *xl = state + (static_cast<size_t>(c * L + seam) * n_cols + static_cast<size_t>(g) * S) * kPacked + li;
         const float *xr = xl + static_cast<size_t>(n_cols) * kPacked - li + ri;
-        double sl = 0.0, sr = 0.0;
-        for (int s = 0; s < S; ++s) {
+        int s = j;
+        for (; s + 3 * J < S; s += 4 * J) {  // four trajectories in flight, summed in index order
+            const float a0 = xl[static_cast<size_t>(s) * kPacked], a1 = xl[static_cast<size_t>(s + J) * kPacked];
+            const float a2 = xl[static_cast<size_t>(s + 2 * J) * kPacked];
+            const float a3 = xl[static_cast<size_t>(s + 3 * J) * kPacked];
+            const float b0 = xr[static_cast<size_t>(s) * kPacked], b1 = xr[static_cast<size_t>(s + J) * kPacked];
+            const float b2 = xr[static_cast<size_t>(s + 2 * J) * kPacked];
+            const float b3 = xr[static_cast<size_t>(s + 3 * J) * kPacked];
+            sl += a0; sl += a1; sl += a2; sl += a3;
+            sr += b0; sr += b1; sr += b2; sr += b3;
+        }
+        for (; s < S; s += J) {
             sl += xl[static_cast<size_t>(s) * kPacked];
             sr += xr[static_cast<size_t>(s) * kPacked];
         }
-        v += fabs(sl - sr) / S;
     }
-    s_acc[threadIdx.x] = v;
+    s_l[t] = sl;
+    s_r[t] = sr;
     __syncthreads();
-    for (int h = 256; h > 0; h >>= 1) {
-        if (static_cast<int>(threadIdx.x) < h) s_acc[threadIdx.x] += s_acc[threadIdx.x + h];
+    double v = 0.0;
+    if (t < NP) {
+        double tl = 0.0, tr = 0.0;
+        for (int jj = 0; jj < J; ++jj) {
+            tl += s_l[jj * NP + t];
+            tr += s_r[jj * NP + t];
+        }
+        v = fabs(tl - tr) / S;
+    }
+    __syncthreads();
+    s_l[t] = v;
+    __syncthreads();
+    for (int h = kMeanAbsThreads / 2; h > 0; h >>= 1) {
+        if (t < h) s_l[t] += s_l[t + h];
         __syncthreads();
     }
-    if (threadIdx.x == 0) out[blockIdx.x] = static_cast<float>(s_acc[0] / NP);
+    if (t == 0) out[blockIdx.x] = static_cast<float>(s_l[0] / NP);
 }
 
 // Mean and max of n values by one workgroup: each lane folds a strided slice
@@ -135,8 +163,8 @@ hipError_t launch_seam_mean_abs(const float *state, int32_t n_chains, int32_t G,
                                 hipStream_t stream) {
     const int64_t blocks = static_cast<int64_t>(n_chains) * (ch.chain_len - 1) * G;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_seam_mean_abs, dim3(static_cast<uint32_t>(blocks)), dim3(512), 0, stream, state, G, S, ch,
-                       out);
+    hipLaunchKernelGGL(k_seam_mean_abs, dim3(static_cast<uint32_t>(blocks)), dim3(kMeanAbsThreads), 0, stream, state,
+                       G, S, ch, out);
     return hipGetLastError();
 }
 
