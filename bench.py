@@ -197,35 +197,39 @@ def sync_ablation(args, wl, n_steps):
                     mid_state = state.view(lay.n_maps, pc.PACKED)[keep_d].clone()
         return traj, mid_state
 
-    def timed(K):
+    def once(K):
         # the whole chain from the C side (one launch per step, no host work in between)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        pc.pc_ddim_sample(state, x0c_d, x0u_d, list(wl.w), lay, n_steps, wl.eta, args.seed, project_every=K)
+        pc.pc_init_state(state, lay, args.seed)
+        ev[0].record()
+        pc.pc_ddim_sample(state, x0c_d, x0u_d, list(wl.w), lay, n_steps, wl.eta, args.seed, project_every=K,
+                          init=False)
+        ev[1].record()
         torch.cuda.synchronize()
-        ms = []
-        for _ in range(args.steps):
-            pc.pc_init_state(state, lay, args.seed)
-            ev[0].record()
-            pc.pc_ddim_sample(state, x0c_d, x0u_d, list(wl.w), lay, n_steps, wl.eta, args.seed, project_every=K,
-                              init=False)
-            ev[1].record()
-            torch.cuda.synchronize()
-            ms.append(ev[0].elapsed_time(ev[1]))
-        return float(np.median(ms)) * 1e-3
+        return ev[0].elapsed_time(ev[1]) * 1e-3
 
     ks = [int(k) for k in args.sync_ablation.split(",")]
+    # timings interleaved over all intervals (K = 0 included), so clock and thermal drift hit all alike
+    samples = {K: [] for K in [0] + ks}
+    for K in samples:
+        once(K)
+    for _ in range(args.steps):
+        for K in samples:
+            samples[K].append(once(K))
+    t_of = {K: float(np.median(v)) for K, v in samples.items()}
     base_traj, base_mid = run(0, True)
-    base_t = timed(0)
+    base_t = t_of[0]
     rows = []
     for K in ks:
         traj, mid_state = run(K, True)
         drift = float(torch.linalg.vector_norm(mid_state - base_mid) / torch.linalg.vector_norm(base_mid))
-        t = timed(K)
+        t = t_of[K]
         rows.append({"K": K, "step_loop_ms": t * 1e3, "wall_ratio": t / base_t,
                      "final_mean_abs_disc": traj[-1], "mean_abs_disc_over_steps": float(np.mean(traj)),
                      "nonoverlap_drift_at_step_%d" % mid: drift})
     print(json.dumps({"metric": "sync-interval ablation", "workload": wl.name, "ddim_steps": n_steps,
-                      "eta": wl.eta, "unsynchronised_mean_abs_disc_over_steps": float(np.mean(base_traj)),
+                      "eta": wl.eta, "unsynchronised_step_loop_ms": base_t * 1e3,
+                      "unsynchronised_mean_abs_disc_over_steps": float(np.mean(base_traj)),
                       "unsynchronised_final_mean_abs_disc": base_traj[-1], "rows": rows,
                       "note": "point-mass stand-in denoiser: every run ends on the reference maps, so final "
                               "discrepancy and drift do not depend on K"}), flush=True)
