@@ -53,6 +53,9 @@ def parse():
     p.add_argument("--sync-ablation", default="",
                    help="comma-separated projection intervals K (0 = never) for a sync-frequency ablation on a "
                         "chain workload; prints one JSON line with a row per K")
+    p.add_argument("--chain-kernels", action="store_true",
+                   help="on a chain workload: time the kernels off the step path (Kabsch stitching, the seam "
+                        "discrepancies, standalone projection) on the final state of one pass; one JSON line")
     p.add_argument("--traffic-summary", default="", metavar="PMC_DIR",
                    help="no GPU: turn the FETCH_SIZE / WRITE_SIZE counter runs under PMC_DIR (copy_<C>/ and "
                         "slab_<C>/ rocprofv3 csv output) into profiles/k_step_indep_<workload>_traffic.json")
@@ -235,6 +238,61 @@ def sync_ablation(args, wl, n_steps):
                               "discrepancy and drift do not depend on K"}), flush=True)
 
 
+def chain_kernels(args, wl, n_steps):
+    """Per-call times of the chain kernels that sit beside the step loop, on the final state
+    and MDS coordinates of one projected pass: HIP events around repeated calls on one stream,
+    median over args.steps groups of 20 calls."""
+    import numpy as np
+    import torch
+
+    import tiled_genome_diffusion_amd as pc
+    from workloads import reference_maps
+
+    if wl.chain_len < 2:
+        raise SystemExit("--chain-kernels needs a chain workload")
+    dev = torch.device("cuda:0")
+    lay = pc.PCLayout(wl.n_regions, wl.n_guidance, wl.n_traj, wl.chain_len, wl.overlap)
+    x0c, x0u = reference_maps(wl, args.seed)
+    x0c_d, x0u_d = torch.from_numpy(x0c).to(dev), torch.from_numpy(x0u).to(dev)
+    state = torch.empty(lay.n_maps * pc.PACKED, dtype=torch.float32, device=dev)
+    pc.pc_ddim_sample(state, x0c_d, x0u_d, list(wl.w), lay, n_steps, wl.eta, args.seed, project_every=1)
+    coords = torch.empty(lay.n_maps * 64 * 3, dtype=torch.float32, device=dev)
+    pc.pc_mds_recover(state, coords)
+    n_chains = wl.n_regions // wl.chain_len
+    n_cols = wl.n_guidance * wl.n_traj
+    n_beads = (wl.chain_len - 1) * (64 - wl.overlap) + 64
+    chain = torch.empty(n_chains * n_cols * n_beads * 3, dtype=torch.float32, device=dev)
+    resid = torch.empty(lay.n_seams * n_cols, dtype=torch.float32, device=dev)
+    rms = torch.empty(lay.n_seams * n_cols, dtype=torch.float32, device=dev)
+    summary = torch.empty(2, dtype=torch.float32, device=dev)
+    mean_abs = torch.empty(lay.n_seams * wl.n_guidance, dtype=torch.float32, device=dev)
+    calls = {
+        "pc_kabsch_stitch": lambda: pc.pc_kabsch_stitch(coords, lay, chain, resid),
+        "pc_seam_mean_abs": lambda: pc.pc_seam_mean_abs(state, lay, mean_abs),
+        "pc_seam_discrepancy": lambda: pc.pc_seam_discrepancy(state, lay, rms, summary),
+        "pc_seam_project": lambda: pc.pc_seam_project(state, lay),
+    }
+    rows = {}
+    for name, fn in calls.items():
+        for _ in range(3):
+            fn()
+        times = []
+        for _ in range(max(1, args.steps)):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record()
+            for _ in range(20):
+                fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            times.append(ev[0].elapsed_time(ev[1]) * 1e3 / 20)
+        rows[name] = float(np.median(times))
+    print(json.dumps({"metric": "chain kernels, microseconds per call", "workload": wl.name,
+                      "chains": n_chains, "joint_samples_per_chain": n_cols, "chain_beads": n_beads,
+                      "us_per_call": rows,
+                      "max_seam_residual": float(resid.max()), "post_projection_rms_max": float(summary[1])}),
+          flush=True)
+
+
 def cpu_baseline(wl, n_steps, seed, target_s):
     """Time the oracle (as it stands) on a bounded sample of the workload."""
     import numpy as np
@@ -322,6 +380,8 @@ def main():
         return None
     if args.sync_ablation:
         return sync_ablation(args, wl, n_steps)
+    if args.chain_kernels:
+        return chain_kernels(args, wl, n_steps)
     dev = torch.device("cuda:0")
     lay = pc.PCLayout(wl.n_regions, wl.n_guidance, wl.n_traj, wl.chain_len, wl.overlap if wl.chain_len > 1 else 0)
     seeds = [int(v) for v in args.seeds.split(",")]

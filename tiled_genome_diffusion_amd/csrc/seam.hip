@@ -36,12 +36,19 @@ __global__ __launch_bounds__(256) void k_seam_project(float *__restrict__ state,
     state[map_r * kPacked + ri] = m;
 }
 
-// One lane per (chain, seam, column): RMS over the seam's pairs, in pair order.
-__global__ __launch_bounds__(256) void k_seam_disc(const float *__restrict__ state, int64_t total, int32_t n_cols,
-                                                   ChainArgs ch, float *__restrict__ rms) {
-    const int64_t sc = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (sc >= total) return;
-    const int L = ch.chain_len, NP = ch.n_pairs, O = ch.overlap;
+// One wavefront per (chain, seam, column): lane l sums the squared
+// differences of pairs l, l + 64, ... in that order, and a DPP tree over the
+// lanes (fixed order, so the result is deterministic) forms the sum over the
+// seam's pairs.
+constexpr int kDiscThreads = 256;
+constexpr int kDiscWaves = kDiscThreads / 64;
+
+__global__ __launch_bounds__(kDiscThreads) void k_seam_disc(const float *__restrict__ state, int64_t total,
+                                                            int32_t n_cols, ChainArgs ch, float *__restrict__ rms) {
+    const int64_t sc = static_cast<int64_t>(blockIdx.x) * kDiscWaves + (threadIdx.x >> 6);
+    if (sc >= total) return;  // uniform over the wavefront
+    const int lane = static_cast<int>(threadIdx.x) & 63;
+    const int L = ch.chain_len, NP = ch.n_pairs;
     const int col = static_cast<int>(sc % n_cols);
     const int64_t cj = sc / n_cols;
     const int64_t c = cj / (L - 1);
@@ -49,13 +56,14 @@ __global__ __launch_bounds__(256) void k_seam_disc(const float *__restrict__ sta
     const float *xl = state + static_cast<size_t>((c * L + j) * n_cols + col) * kPacked;
     const float *xr = xl + static_cast<size_t>(n_cols) * kPacked;
     float acc = 0.f;
-    int p = 0;
-    for (int pp = 0; pp < O; ++pp)
-        for (int qq = pp + 1; qq < O; ++qq, ++p) {
-            const float d = xl[packed_index(kBeads - O + pp, kBeads - O + qq)] - xr[packed_index(pp, qq)];
-            acc = fmaf(d, d, acc);
-        }
-    rms[sc] = sqrtf(acc / static_cast<float>(NP));
+    for (int p = lane; p < NP; p += 64) {
+        int li, ri;
+        pair_indices(p, ch.overlap, li, ri);
+        const float d = xl[li] - xr[ri];
+        acc = fmaf(d, d, acc);
+    }
+    const float sum = wave_sum(acc);
+    if (lane == 0) rms[sc] = sqrtf(sum / static_cast<float>(NP));
 }
 
 // Paper-form seam discrepancy: one 1024-lane workgroup per (chain, seam,
@@ -122,20 +130,36 @@ __global__ __launch_bounds__(kMeanAbsThreads) void k_seam_mean_abs(const float *
 }
 
 // Mean and max of n values by one workgroup: each lane folds a strided slice
-// in index order, then a fixed tree over the lanes.  Deterministic.
-__global__ __launch_bounds__(256) void k_mean_max(const float *__restrict__ v, int64_t n, float *__restrict__ out) {
-    __shared__ double s_sum[256];
-    __shared__ float s_max[256];
+// in index order (eight loads in flight), then a fixed tree over the lanes.
+// Deterministic.
+constexpr int kMeanMaxThreads = 1024;
+
+__global__ __launch_bounds__(kMeanMaxThreads) void k_mean_max(const float *__restrict__ v, int64_t n,
+                                                              float *__restrict__ out) {
+    __shared__ double s_sum[kMeanMaxThreads];
+    __shared__ float s_max[kMeanMaxThreads];
+    constexpr int T = kMeanMaxThreads;
     double acc = 0.0;
     float mx = 0.f;
-    for (int64_t i = threadIdx.x; i < n; i += 256) {
+    int64_t i = threadIdx.x;
+    for (; i + 7 * T < n; i += 8 * T) {
+        float x[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x[k] = v[i + k * T];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            acc += x[k];
+            mx = fmaxf(mx, x[k]);
+        }
+    }
+    for (; i < n; i += T) {
         acc += v[i];
         mx = fmaxf(mx, v[i]);
     }
     s_sum[threadIdx.x] = acc;
     s_max[threadIdx.x] = mx;
     __syncthreads();
-    for (int h = 128; h > 0; h >>= 1) {
+    for (int h = T / 2; h > 0; h >>= 1) {
         if (static_cast<int>(threadIdx.x) < h) {
             s_sum[threadIdx.x] += s_sum[threadIdx.x + h];
             s_max[threadIdx.x] = fmaxf(s_max[threadIdx.x], s_max[threadIdx.x + h]);
@@ -172,14 +196,14 @@ hipError_t launch_seam_discrepancy(const float *state, int32_t n_chains, int32_t
                                    float *summary, hipStream_t stream) {
     const int64_t total = static_cast<int64_t>(n_chains) * (ch.chain_len - 1) * n_cols;
     if (total > 0) {
-        const int64_t blocks = (total + 255) / 256;
-        hipLaunchKernelGGL(k_seam_disc, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream, state, total,
-                           n_cols, ch, rms);
+        const int64_t blocks = (total + kDiscWaves - 1) / kDiscWaves;
+        hipLaunchKernelGGL(k_seam_disc, dim3(static_cast<uint32_t>(blocks)), dim3(kDiscThreads), 0, stream, state,
+                           total, n_cols, ch, rms);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (summary) {
-        hipLaunchKernelGGL(k_mean_max, dim3(1), dim3(256), 0, stream, rms, total, summary);
+        hipLaunchKernelGGL(k_mean_max, dim3(1), dim3(kMeanMaxThreads), 0, stream, rms, total, summary);
         return hipGetLastError();
     }
     return hipSuccess;
