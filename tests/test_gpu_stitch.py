@@ -19,23 +19,26 @@ def _orth(rng, reflect):
     return q
 
 
-def test_stitch_synthetic_rigid_motions():
+@pytest.mark.parametrize("L,O,n_chains,S", [(6, 12, 3, 4), (65, 4, 2, 3), (130, 12, 1, 2), (1024, 32, 1, 1)],
+                         ids=["L6-O12", "L65-O4", "L130-O12", "L1024-O32"])
+def test_stitch_synthetic_rigid_motions(L, O, n_chains, S):
+    """Per-tile random rotations, reflections and shifts undone; chains longer than 64
+    tiles cross the 64-tile chunks the fits are composed in, and 1024 is the longest
+    chain the entry point accepts."""
     torch, dev = torch_dev()
-    rng = np.random.default_rng(0)
-    L, O, n_chains, S = 6, 12, 3, 4
+    rng = np.random.default_rng(L * 100 + O)
+    stride = 64 - O
     lay = pc.PCLayout(n_chains * L, 1, S, L, O)
-    say("stitch: per-tile random rigid motions and reflections")
+    say(f"stitch: per-tile random rigid motions and reflections, L={L} O={O} chains={n_chains} S={S}")
     coords = np.zeros((n_chains * L, 1, S, 64, 3), dtype=np.float32)
-    truth = {}
     for c in range(n_chains):
         for s in range(S):
-            walk = random_walk((L - 1) * 52 + 64, walk_rng(c, s, 77), None)
-            truth[c, s] = walk
+            walk = random_walk((L - 1) * stride + 64, walk_rng(c, s, 77), None)
             for k in range(L):
-                t = walk[k * 52:k * 52 + 64]
+                t = walk[k * stride:k * stride + 64]
                 coords[c * L + k, 0, s] = t @ _orth(rng, (k + s) % 2 == 1) + rng.standard_normal(3) * 5
     cd = torch.from_numpy(coords.reshape(-1)).to(dev)
-    nb = (L - 1) * 52 + 64
+    nb = (L - 1) * stride + 64
     chain = torch.empty(n_chains * S * nb * 3, dtype=torch.float32, device=dev)
     resid = torch.empty(n_chains * (L - 1) * S, dtype=torch.float32, device=dev)
     pc.pc_kabsch_stitch(cd, lay, chain, resid)

@@ -5,35 +5,37 @@
 // translation that best superpose its first O beads on tile k-1's last O
 // beads.  The best fit onto a rigidly moved target is the moved best fit, so
 // with F_k the fit of raw tile k onto raw tile k-1 (row vectors:
-// F_k(x) = x R_k + t_k) the aligned frame of tile k is T_k = T_{k-1} o F_k,
-// T_0 = identity: M_k = R_k M_{k-1}, u_k = t_k M_{k-1} + u_{k-1}.  Hence one
-// 1024-lane workgroup per joint sample works in three phases:
-//   1. each of its 16 wavefronts fits seams k = 1..L-1 in turn (lane i < O
-//      holds shared bead i of both tiles): centroids, H = x^T y of the centred
-//      beads, R_k = the orthogonal polar factor of H (= U V^T for
-//      H = U S V^T; reflections allowed, since distance maps carry no
-//      chirality) by Higham's scaled Newton iteration, and the seam's
-//      residual, the RMS distance over the shared beads after
-//      the fit, which no rigid motion of both tiles changes;
-//   2. one lane composes the L transforms in order (LDS);
-//   3. the wavefronts move their tiles' beads into the chain frame; a shared
-//      bead takes the mean of its two aligned positions (written by the later
-//      tile).
+// F_k(x) = x R_k + t_k) the aligned frame of tile k is
+// T_k = F_1 o F_2 o ... o F_k, an inclusive scan under composition.  One
+// 256-lane workgroup per joint sample works in three phases:
+//   1. the tiles are taken in chunks of 64, one lane per tile: lane k fits
+//      seam k on its own (centroids and H = x^T y of the centred shared
+//      beads in one shifted pass, R_k = the orthogonal polar factor of H by
+//      Higham's scaled Newton iteration, reflections allowed since distance
+//      maps carry no chirality, then the seam's residual, the RMS distance
+//      over the shared beads after the fit, which no rigid motion of both
+//      tiles changes), and a wavefront scan composes the chunk's fits;
+//   2. the chunks' scans are joined by carrying each chunk's total into the
+//      next (LDS, at most 16 chunks);
+//   3. the wavefronts move their tiles' beads into the chain frame, one lane
+//      per bead; a shared bead takes the mean of its two aligned positions
+//      (written by the later tile).
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace pc {
 namespace {
 
-constexpr int kStitchThreads = 1024;
+constexpr int kStitchThreads = 256;
 constexpr int kStitchWaves = kStitchThreads / 64;
+constexpr int kStitchMaxChunks = 16;  // chains of up to 1024 tiles
 
 __device__ __forceinline__ float det3(const float (&m)[3][3]) {
     return m[0][0] * (m[1][1] * m[2][2] - m[1][2] * m[2][1]) - m[0][1] * (m[1][0] * m[2][2] - m[1][2] * m[2][0]) +
            m[0][2] * (m[1][0] * m[2][1] - m[1][1] * m[2][0]);
 }
 
-// Orthogonal polar factor of a non-singular 3x3 (wave-uniform values) by
+// Orthogonal polar factor of a non-singular 3x3 (one per lane) by
 // Higham's scaled Newton iteration X <- (g X + X^{-T} / g) / 2, X^{-T} the
 // cofactor matrix over det X, g = (|X^{-1}|_F / |X|_F)^(1/2) for the first
 // steps and 1 after.  The iteration corrects its own rounding, so the
@@ -83,102 +85,173 @@ __device__ __forceinline__ void apply(const float *t, const float (&x)[3], float
     for (int b = 0; b < 3; ++b) y[b] = fmaf(x[0], t[b], fmaf(x[1], t[3 + b], fmaf(x[2], t[6 + b], t[9 + b])));
 }
 
+// out = a o b (b first, then a): x (M_b M_a) + (u_b M_a + u_a).  out may alias b.
+__device__ __forceinline__ void compose(const float (&a)[12], float (&b)[12]) {
+    float r[12];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)  // rows 0..2 of M_b, then u_b (row 3, plus u_a)
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+            r[3 * i + j] = fmaf(b[3 * i], a[j], fmaf(b[3 * i + 1], a[3 + j], fmaf(b[3 * i + 2], a[6 + j],
+                                                                             i == 3 ? a[9 + j] : 0.f)));
+#pragma unroll
+    for (int e = 0; e < 12; ++e) b[e] = r[e];
+}
+
+__device__ __forceinline__ void identity(float (&t)[12]) {
+#pragma unroll
+    for (int e = 0; e < 12; ++e) t[e] = (e == 0 || e == 4 || e == 8) ? 1.f : 0.f;
+}
+
+// Fit of O beads x (tile k's first) onto y (tile k-1's last): t = (R, shift) with
+// y ~ x R + shift; returns the mean squared distance after the fit.  The sums
+// are shifted by each block's first bead, so centring loses nothing to
+// cancellation.
+__device__ float fit(const float *x, const float *y, int O, float (&t)[12]) {
+    float x0[3], y0[3], sx[3] = {0.f, 0.f, 0.f}, sy[3] = {0.f, 0.f, 0.f}, h[3][3] = {};
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        x0[a] = x[a];
+        y0[a] = y[a];
+    }
+    for (int i = 1; i < O; ++i) {
+        float dx[3], dy[3];
+#pragma unroll
+        for (int a = 0; a < 3; ++a) {
+            dx[a] = x[3 * i + a] - x0[a];
+            dy[a] = y[3 * i + a] - y0[a];
+            sx[a] += dx[a];
+            sy[a] += dy[a];
+        }
+#pragma unroll
+        for (int a = 0; a < 3; ++a)
+#pragma unroll
+            for (int b = 0; b < 3; ++b) h[a][b] = fmaf(dx[a], dy[b], h[a][b]);
+    }
+    const float inv = 1.f / static_cast<float>(O);
+    float xm[3], ym[3];
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        xm[a] = sx[a] * inv;  // centroid offsets from bead 0
+        ym[a] = sy[a] * inv;
+    }
+#pragma unroll
+    for (int a = 0; a < 3; ++a)
+#pragma unroll
+        for (int b = 0; b < 3; ++b) h[a][b] = fmaf(-static_cast<float>(O) * xm[a], ym[b], h[a][b]);
+    polar3(h);
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        xm[a] += x0[a];
+        ym[a] += y0[a];
+    }
+#pragma unroll
+    for (int a = 0; a < 3; ++a)
+#pragma unroll
+        for (int b = 0; b < 3; ++b) t[3 * a + b] = h[a][b];
+#pragma unroll
+    for (int b = 0; b < 3; ++b) t[9 + b] = ym[b] - (xm[0] * h[0][b] + xm[1] * h[1][b] + xm[2] * h[2][b]);
+    float r2 = 0.f;
+    for (int i = 0; i < O; ++i) {
+        const float p[3] = {x[3 * i], x[3 * i + 1], x[3 * i + 2]};
+        float q[3];
+        apply(t, p, q);
+#pragma unroll
+        for (int a = 0; a < 3; ++a) {
+            const float d = q[a] - y[3 * i + a];
+            r2 = fmaf(d, d, r2);
+        }
+    }
+    return r2 * inv;
+}
+
 __global__ __launch_bounds__(kStitchThreads) void k_stitch(const float *__restrict__ coords, int32_t G, int32_t S,
                                                            ChainArgs ch, float *__restrict__ chain,
                                                            float *__restrict__ resid) {
-    extern __shared__ float s_t[];  // [L][12]: F_k after phase 1, T_k after phase 2
+    extern __shared__ float s_t[];  // [L][12]: chunk-local scans, then T_k; [16][12]: chunk totals, then carries
     const int wave = static_cast<int>(threadIdx.x) >> 6, lane = static_cast<int>(threadIdx.x) & 63;
     const int n_cols = G * S;
     const int c = static_cast<int>(blockIdx.x) / n_cols;
     const int gs = static_cast<int>(blockIdx.x) - c * n_cols;
     const int L = ch.chain_len, O = ch.overlap, stride = kBeads - O;
     const int n_beads = (L - 1) * stride + kBeads;
-    auto bead = [&](int k, int i) {  // raw coordinates of bead i of tile k
-        const float *p = coords + ((static_cast<size_t>(c * L + k) * n_cols + gs) * kBeads + i) * 3;
-        return p;
+    const int n_chunks = (L + 63) >> 6;
+    float *s_tot = s_t + 12 * L;
+    auto tile = [&](int k) {  // raw coordinates of tile k, [64][3]
+        return coords + (static_cast<size_t>(c * L + k) * n_cols + gs) * kBeads * 3;
     };
-    const bool shared = lane < O;
 
-    // 1. pairwise fits of raw tile k onto raw tile k-1
-    for (int k = 1 + wave; k < L; k += kStitchWaves) {
-        float x[3] = {0.f, 0.f, 0.f}, y[3] = {0.f, 0.f, 0.f};
-        if (shared) {
-            const float *px = bead(k, lane), *py = bead(k - 1, stride + lane);
+    // 1. per-lane fits, scanned within each 64-tile chunk
+    for (int j = wave; j < n_chunks; j += kStitchWaves) {
+        const int k = 64 * j + lane;
+        float t[12];
+        identity(t);
+        if (k >= 1 && k < L) {
+            const float r2 = fit(tile(k), tile(k - 1) + stride * 3, O, t);
+            resid[(static_cast<size_t>(c) * (L - 1) + k - 1) * n_cols + gs] = sqrtf(r2);
+        }
+        // inclusive scan: t_k <- t_{k-d} o t_k
 #pragma unroll
-            for (int a = 0; a < 3; ++a) {
-                x[a] = px[a];
-                y[a] = py[a];
+        for (int d = 1; d < 64; d <<= 1) {
+            float o[12];
+#pragma unroll
+            for (int e = 0; e < 12; ++e) o[e] = __shfl_up(t[e], d, 64);
+            if (lane >= d) compose(o, t);
+        }
+        if (k < L) {
+#pragma unroll
+            for (int e = 0; e < 12; ++e) s_t[12 * k + e] = t[e];
+        }
+        if (lane == 63) {
+#pragma unroll
+            for (int e = 0; e < 12; ++e) s_tot[12 * j + e] = t[e];
+        }
+    }
+    __syncthreads();
+
+    // 2. carries: C_0 = identity, C_{j+1} = C_j o total_j (stored over the totals)
+    if (threadIdx.x == 0 && n_chunks > 1) {
+        float cur[12];
+        identity(cur);
+        for (int j = 0; j < n_chunks; ++j) {
+            float nxt[12];
+#pragma unroll
+            for (int e = 0; e < 12; ++e) nxt[e] = s_tot[12 * j + e];
+            compose(cur, nxt);
+#pragma unroll
+            for (int e = 0; e < 12; ++e) {
+                s_tot[12 * j + e] = cur[e];
+                cur[e] = nxt[e];
             }
         }
-        float xm[3], ym[3];
-#pragma unroll
-        for (int a = 0; a < 3; ++a) {
-            xm[a] = wave_sum(x[a]) / O;
-            ym[a] = wave_sum(y[a]) / O;
-        }
-        float h[3][3];
-#pragma unroll
-        for (int a = 0; a < 3; ++a)
-#pragma unroll
-            for (int b = 0; b < 3; ++b) h[a][b] = wave_sum(shared ? (x[a] - xm[a]) * (y[b] - ym[b]) : 0.f);
-        polar3(h);
-        float fx[3];
-#pragma unroll
-        for (int b = 0; b < 3; ++b)
-            fx[b] = (x[0] - xm[0]) * h[0][b] + (x[1] - xm[1]) * h[1][b] + (x[2] - xm[2]) * h[2][b] + ym[b];
-        float d2 = 0.f;
-#pragma unroll
-        for (int a = 0; a < 3; ++a) d2 += (fx[a] - y[a]) * (fx[a] - y[a]);
-        const float r2 = wave_sum(shared ? d2 : 0.f) / O;
-        if (lane == 0) {
-            resid[(static_cast<size_t>(c) * (L - 1) + k - 1) * n_cols + gs] = sqrtf(r2);
-            float *t = s_t + 12 * k;
-#pragma unroll
-            for (int a = 0; a < 3; ++a)
-#pragma unroll
-                for (int b = 0; b < 3; ++b) t[3 * a + b] = h[a][b];
-            // t_k = ym - xm R
-#pragma unroll
-            for (int b = 0; b < 3; ++b) t[9 + b] = ym[b] - (xm[0] * h[0][b] + xm[1] * h[1][b] + xm[2] * h[2][b]);
-        }
     }
     __syncthreads();
-
-    // 2. compose: T_0 = identity, M_k = R_k M_{k-1}, u_k = t_k M_{k-1} + u_{k-1}
-    if (threadIdx.x == 0) {
-        float m[9] = {1.f, 0.f, 0.f, 0.f, 1.f, 0.f, 0.f, 0.f, 1.f}, u[3] = {0.f, 0.f, 0.f};
+    if (n_chunks > 1) {
+        for (int k = 64 + static_cast<int>(threadIdx.x); k < L; k += kStitchThreads) {
+            float cj[12], t[12];
 #pragma unroll
-        for (int e = 0; e < 9; ++e) s_t[e] = m[e];
-        s_t[9] = s_t[10] = s_t[11] = 0.f;
-        for (int k = 1; k < L; ++k) {
-            float *t = s_t + 12 * k;
-            float nm[9], nu[3];
+            for (int e = 0; e < 12; ++e) {
+                cj[e] = s_tot[12 * (k >> 6) + e];
+                t[e] = s_t[12 * k + e];
+            }
+            compose(cj, t);
 #pragma unroll
-            for (int a = 0; a < 3; ++a)
-#pragma unroll
-                for (int b = 0; b < 3; ++b)
-                    nm[3 * a + b] = fmaf(t[3 * a], m[b], fmaf(t[3 * a + 1], m[3 + b], t[3 * a + 2] * m[6 + b]));
-#pragma unroll
-            for (int b = 0; b < 3; ++b)
-                nu[b] = fmaf(t[9], m[b], fmaf(t[10], m[3 + b], fmaf(t[11], m[6 + b], u[b])));
-#pragma unroll
-            for (int e = 0; e < 9; ++e) t[e] = m[e] = nm[e];
-#pragma unroll
-            for (int b = 0; b < 3; ++b) t[9 + b] = u[b] = nu[b];
+            for (int e = 0; e < 12; ++e) s_t[12 * k + e] = t[e];
         }
+        __syncthreads();
     }
-    __syncthreads();
 
     // 3. move every tile into the chain frame
     float *out = chain + (static_cast<size_t>(c) * n_cols + gs) * n_beads * 3;
+    const bool shared = lane < O;
     for (int k = wave; k < L; k += kStitchWaves) {
-        const float *p = bead(k, lane);
+        const float *p = tile(k) + lane * 3;
         const float x[3] = {p[0], p[1], p[2]};
         float cur[3];
         apply(s_t + 12 * k, x, cur);
         float *dst = out + (static_cast<size_t>(k) * stride + lane) * 3;
         if (k > 0 && shared) {  // mean with tile k-1's aligned copy of the same bead
-            const float *q = bead(k - 1, stride + lane);
+            const float *q = tile(k - 1) + (stride + lane) * 3;
             const float y[3] = {q[0], q[1], q[2]};
             float prev[3];
             apply(s_t + 12 * (k - 1), y, prev);
@@ -197,7 +270,8 @@ hipError_t launch_stitch(const float *coords, int32_t n_chains, int32_t G, int32
                          float *resid, hipStream_t stream) {
     const int64_t blocks = static_cast<int64_t>(n_chains) * G * S;
     if (blocks == 0) return hipSuccess;
-    const size_t lds = static_cast<size_t>(ch.chain_len) * 12 * sizeof(float);
+    if (ch.chain_len > 64 * kStitchMaxChunks) return hipErrorInvalidValue;
+    const size_t lds = static_cast<size_t>(ch.chain_len + kStitchMaxChunks) * 12 * sizeof(float);
     hipLaunchKernelGGL(k_stitch, dim3(static_cast<uint32_t>(blocks)), dim3(kStitchThreads), lds, stream, coords, G, S,
                        ch, chain, resid);
     return hipGetLastError();
