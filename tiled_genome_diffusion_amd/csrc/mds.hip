@@ -8,7 +8,7 @@
 //      grand mean (wavefront reduction); row i of B stays in VGPRs.
 //   3. Block-4 subspace iteration with Rayleigh-Ritz: Q <- orth(Z) by
 //      modified Gram-Schmidt (a column that cancels is projected twice),
-//      Z = B Q (Q broadcast from LDS, 256 FMAs per lane), H = Q^T Z by DPP
+//      Z = B Q (64 4x4x1 MFMA steps, Q^T read from LDS), H = Q^T Z by DPP
 //      wavefront reductions, a 4x4 Jacobi eigensolve (wave-uniform values,
 //      eigenvector rows spread over lanes 0..3), Ritz vectors V = Q W,
 //      Z W = B V and the residuals ||B V_k - theta_k V_k|| of the three
@@ -27,6 +27,7 @@
 //      largest-magnitude entry is positive (lowest index on ties).
 #include "common.hpp"
 #include "launch.hpp"
+#include "mds_start.hpp"
 
 namespace pc {
 namespace {
@@ -34,16 +35,9 @@ namespace {
 constexpr int kLanes = 64;
 constexpr int kBlk = 4;
 
-// Fixed pseudo-random start vectors (an integer hash of (bead, column)).
-__device__ __forceinline__ float start_vec(int i, int k) {
-    uint32_t x = static_cast<uint32_t>(i) * 0x9E3779B1u + static_cast<uint32_t>(k) * 0x85EBCA77u + 0x165667B1u;
-    x ^= x >> 16;
-    x *= 0x7FEB352Du;
-    x ^= x >> 15;
-    x *= 0x846CA68Bu;
-    x ^= x >> 16;
-    return static_cast<float>(x >> 8) * 0x1p-23f - 1.0f;
-}
+// Column k of the start block for bead i (orthonormal, orthogonal to the
+// all-ones vector; mds_start.hpp).
+__device__ __forceinline__ float start_vec(int i, int k) { return kMdsStart[i][k]; }
 
 // Cyclic Jacobi on a symmetric 4x4 (values identical in every lane).  The
 // rotation that zeroes h_pq uses t = sgn(th) / (|th| + sqrt(th^2 + 1)) with
@@ -169,26 +163,38 @@ __device__ __forceinline__ void project_out(const Deflation &dfl, int lane, floa
 }
 
 // z = B q for the four per-lane columns q (row `lane` of B in b, whose
-// diagonal entry is off by diag_err).
+// diagonal entry is off by diag_err), on the matrix cores: 64 rank-1 steps of
+// v_mfma_f32_4x4x1f32 (16 blocks of 4x4).  Block c / 4 of step k multiplies
+// A = (q_k0 .. q_k3) (lane 4 blk + r supplies q_kr, read from Q^T in LDS) by
+// B = (b_{4 blk + j, k})_j (lane l supplies its own b[k] = B_lk = B_kl), so
+// output register r of lane l accumulates sum_k q_kr B_kl = (B q)_lr: lane l
+// ends with row l of B Q.  Four accumulators take the steps in turn, so
+// consecutive steps do not wait on each other.
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ void block_matvec(const float (&b)[kBeads], float diag_err, int lane,
                                              const float (&q)[kBlk], float4 *s_q, float (&z)[kBlk]) {
-    s_q[lane] = make_float4(q[0], q[1], q[2], q[3]);
+    float *s_qt = reinterpret_cast<float *>(s_q);  // Q^T: column c at s_qt[c * 64 + bead]
+#pragma unroll
+    for (int c = 0; c < kBlk; ++c) s_qt[c * kBeads + lane] = q[c];
     __syncthreads();
+    const float4 *qa = reinterpret_cast<const float4 *>(s_qt + (lane & 3) * kBeads);
+    f32x4v acc[4];
 #pragma unroll
-    for (int k = 0; k < kBlk; ++k) z[k] = 0.f;
+    for (int e = 0; e < 4; ++e) acc[e] = f32x4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < kBeads; ++j) {
-        const float4 qj = s_q[j];
-        z[0] = fmaf(b[j], qj.x, z[0]);
-        z[1] = fmaf(b[j], qj.y, z[1]);
-        z[2] = fmaf(b[j], qj.z, z[2]);
-        z[3] = fmaf(b[j], qj.w, z[3]);
-        // keep at most 8 broadcast rows of Q in flight (otherwise all 64
-        // LDS reads are hoisted and the register file overflows)
-        if (j % 8 == 7) __builtin_amdgcn_sched_barrier(0);
+    for (int k4 = 0; k4 < kBeads / 4; ++k4) {
+        const float4 a = qa[k4];  // q_{4 k4 + e, lane & 3}
+        acc[0] = __builtin_amdgcn_mfma_f32_4x4x1f32(a.x, b[4 * k4 + 0], acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_4x4x1f32(a.y, b[4 * k4 + 1], acc[1], 0, 0, 0);
+        acc[2] = __builtin_amdgcn_mfma_f32_4x4x1f32(a.z, b[4 * k4 + 2], acc[2], 0, 0, 0);
+        acc[3] = __builtin_amdgcn_mfma_f32_4x4x1f32(a.w, b[4 * k4 + 3], acc[3], 0, 0, 0);
+        // keep at most two rows of Q^T in flight (hoisting all 16 LDS reads
+        // would overflow the register file)
+        if (k4 % 2 == 1) __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int k = 0; k < kBlk; ++k) z[k] = fmaf(-diag_err, q[k], z[k]);
+    for (int k = 0; k < kBlk; ++k) z[k] = fmaf(-diag_err, q[k], (acc[0][k] + acc[1][k]) + (acc[2][k] + acc[3][k]));
     __syncthreads();
 }
 
@@ -202,7 +208,8 @@ __device__ __forceinline__ bool may_hide(const float (&d)[kBlk], float rho) {
 
 // Block-4 subspace iteration on P B P, P the projector onto the complement of
 // the deflated vectors (none at first).  Each iteration orthonormalises the
-// last product (q <- MGS(z), starting from fixed pseudo-random vectors),
+// last product (q <- MGS(z); the first pass starts from the fixed orthonormal
+// start block, later passes from its projection onto the complement),
 // multiplies again (z <- P B q), and from the second product on takes the
 // Rayleigh-Ritz pairs of (q, z): H = q^T z, H = W diag(theta) W^T, vec = q W,
 // residual ||z W - theta vec||.
@@ -221,11 +228,14 @@ __device__ __forceinline__ bool may_hide(const float (&d)[kBlk], float rho) {
 __device__ __forceinline__ void subspace(const float (&b)[kBeads], float diag_err, Deflation &dfl, int32_t max_iters,
                                          int lane, float4 *s_q, float (&theta)[kBlk], float (&vec)[kBlk]) {
     float q[kBlk], z[kBlk];
-#pragma unroll
-    for (int k = 0; k < kBlk; ++k) z[k] = start_vec(lane, k);
     int pass = 0, steps = 0;
     for (int it = 0;; ++it) {
-        orthonormalise(lane, z, q);
+        if (it == 0 && pass == 0) {  // the start block is orthonormal already
+#pragma unroll
+            for (int k = 0; k < kBlk; ++k) q[k] = start_vec(lane, k);
+        } else {
+            orthonormalise(lane, z, q);
+        }
         block_matvec(b, diag_err, lane, q, s_q, z);
         project_out(dfl, lane, z);
         if (it == 0) continue;  // the first product only seeds the subspace
