@@ -151,3 +151,23 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros(16 * 2016)
     with pytest.raises(ValueError):
         pc.pc_init_state(x, pc.PCLayout(1, 2, 8), 0)
+
+
+def test_mds_start_block_is_current_and_orthonormal(repo_root):
+    """The committed start block of the MDS iteration is what its generator writes,
+    orthonormal and orthogonal to the all-ones vector (the null vector of a doubly
+    centred matrix) to float32 rounding."""
+    import importlib.util
+
+    csrc = os.path.join(repo_root, "tiled_genome_diffusion_amd", "csrc")
+    spec = importlib.util.spec_from_file_location("mds_start", os.path.join(csrc, "mds_start.py"))
+    gen = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(gen)
+    with open(os.path.join(csrc, "mds_start.hpp")) as f:
+        text = f.read()
+    got = np.array([float(v) for v in re.findall(r"(-?[0-9.]+e[-+][0-9]+)f", text)], dtype=np.float32)
+    assert got.shape == (64 * 4,)
+    q = got.reshape(64, 4).astype(np.float64)
+    assert np.array_equal(got.reshape(64, 4), gen.start_block())
+    assert np.abs(q.T @ q - np.eye(4)).max() < 1e-6
+    assert np.abs(q.sum(axis=0)).max() < 1e-6
