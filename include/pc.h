@@ -258,7 +258,8 @@ PC_API pc_status pc_mds_recover(const float *maps, int64_t n_maps, float *coords
  * The seams are fitted independently in their tiles' own frames and the fits
  * composed along the chain, which equals fitting each tile onto the already
  * aligned one (a rigid motion of the target moves the best fit with it).
- * Errors: NULL pointers; bad layout; chain_len outside 2..1024.
+ * Errors: NULL pointers; bad layout; chain_len outside 2..1024; overlap below
+ * 4 (three or fewer shared beads are always coplanar).
  */
 PC_API pc_status pc_kabsch_stitch(const float *coords, const pc_layout *layout, float *chain, float *residual,
                                   void *stream);

@@ -140,6 +140,8 @@ def test_other_validation(lib):
     assert lib.pc_kabsch_stitch(FAKE, ctypes.byref(lay), FAKE, FAKE, None) == -2            # no chains
     long_chain = _lay(R=2048, G=1, S=1, L=2048, O=12)
     assert lib.pc_kabsch_stitch(FAKE, ctypes.byref(long_chain), FAKE, FAKE, None) == -2     # chain_len > 1024
+    short_seam = _lay(R=4, G=1, S=1, L=4, O=3)
+    assert lib.pc_kabsch_stitch(FAKE, ctypes.byref(short_seam), FAKE, FAKE, None) == -2     # coplanar seams
     assert lib.pc_philox_fill(ctypes.c_void_p(4097), ctypes.byref(lay), 0, 0, None) == -3
     assert lib.pc_ddim_sample(FAKE, FAKE, FAKE, W, ctypes.byref(lay), 7, 1000, 1e-4, 0.02, 1.0, 0, 0, 1, None) == -4
     assert lib.pc_ddim_sample(FAKE, FAKE, FAKE, W, ctypes.byref(lay), 50, 1000, 1e-4, 0.02, 1.0, 0, 1, 1, None) == -4

@@ -348,6 +348,8 @@ pc_status pc_kabsch_stitch(const float *coords, const pc_layout *layout, float *
     if (st != PC_OK) return st;
     if (layout->chain_len < 2 || layout->chain_len > 1024)
         return fail(PC_ERR_SHAPE, "stitching needs 2 <= chain_len <= 1024 (got %d)", layout->chain_len);
+    if (layout->overlap < 4)  // three or fewer points are always coplanar: the fit is not unique
+        return fail(PC_ERR_SHAPE, "stitching needs overlap >= 4 (got %d)", layout->overlap);
     if (!aligned16(coords) || !aligned16(chain) || !aligned16(residual))
         return fail(PC_ERR_ALIGN, "device arrays must be 16-byte aligned");
     return hip_status(pc::launch_stitch(coords, layout->n_regions / layout->chain_len, layout->n_guidance,
