@@ -43,6 +43,8 @@ def parse():
                    help="base seeds the timed passes cycle through (inputs and noise); per-seed rates are reported")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target duration of the oracle baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-procs", type=int, default=0,
+                   help="with --cpu-only: also time the oracle in this many processes over disjoint blocks")
     p.add_argument("--cpu-only", action="store_true",
                    help="no GPU: print only the oracle baseline of the workload (one JSON line)")
     p.add_argument("--eps-buffers", action="store_true",
@@ -293,22 +295,25 @@ def chain_kernels(args, wl, n_steps):
           flush=True)
 
 
-def cpu_baseline(wl, n_steps, seed, target_s):
-    """Time the oracle (as it stands) on a bounded sample of the workload."""
+def _oracle_block(name, n_steps, seed, lo, n):
+    """The oracle on one block of a workload, one BLAS thread: maps lo .. lo+n-1 of an
+    independent workload, or joint-sample columns lo .. lo+n-1 (column c = weight
+    c // S, trajectory c % S, every tile) of a chain.  Returns (maps, sampling s, MDS s)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     from oracle import mds, sampler
-    from workloads import reference_maps
+    from workloads import get, reference_maps
 
+    wl = get(name)
     G, S = wl.n_guidance, wl.n_traj
-
-    def run(n_maps):
+    with threadpool_limits(limits=1):
         if wl.chain_len == 1:
-            idx = np.arange(n_maps)
+            idx = np.arange(lo, lo + n)
             r = idx // (G * S)
-            x0c, x0u = reference_maps(wl, seed, regions=sorted(set(r.tolist())))
-            pos = {v: k for k, v in enumerate(sorted(set(r.tolist())))}
+            regions = sorted(set(r.tolist()))
+            x0c, x0u = reference_maps(wl, seed, regions=regions)
+            pos = {v: k for k, v in enumerate(regions)}
             rr = np.array([pos[v] for v in r])
             w = np.asarray(wl.w)[(idx // S) % G]
             t0 = time.perf_counter()
@@ -317,31 +322,61 @@ def cpu_baseline(wl, n_steps, seed, target_s):
         else:
             x0c, x0u = reference_maps(wl, seed)
             L = wl.chain_len
-            cols = max(1, n_maps // L)
-            tids = np.array([[(k * G + 0) * S + s for s in range(cols)] for k in range(L)])
-            w = np.full(cols, wl.w[0])
+            cols = np.arange(lo, lo + n)
+            tids = np.array([[(k * G + c // S) * S + c % S for c in cols] for k in range(L)])
+            w = np.asarray(wl.w)[cols // S]
             t0 = time.perf_counter()
             fin, _, _, _ = sampler.run_chain(x0c[:L], x0u[:L], w, tids, seed, n_steps, wl.eta, wl.overlap)
             t1 = time.perf_counter()
             fin = fin.reshape(-1, 2016)
-            n_maps = fin.shape[0]
         for m in fin:
             mds.classical_mds(m)
         t2 = time.perf_counter()
-        return n_maps, t1 - t0, t2 - t1
+    return fin.shape[0], t1 - t0, t2 - t1
 
-    with threadpool_limits(limits=1):
-        n = 16
-        n_maps, ts, tm = run(n)
-        while ts + tm < target_s / 4 and n < wl.n_maps:
-            n = min(wl.n_maps, n * 4)
-            n_maps, ts, tm = run(n)
+
+def _oracle_block_star(args):
+    return _oracle_block(*args)
+
+
+def cpu_baseline(wl, n_steps, seed, target_s):
+    """Time the oracle (as it stands) on a bounded sample of the workload, one thread."""
+    L = wl.chain_len
+    n = 16
+    n_maps, ts, tm = _oracle_block(wl.name, n_steps, seed, 0, n if L == 1 else max(1, n // L))
+    while ts + tm < target_s / 4 and n < wl.n_maps:
+        n = min(wl.n_maps, n * 4)
+        n_maps, ts, tm = _oracle_block(wl.name, n_steps, seed, 0, n if L == 1 else max(1, n // L))
     return {"value": n_maps * n_steps / (ts + tm), "unit": "trajectory-steps/s", "cores": 1, "kind": "oracle",
             "sample": f"{n_maps} of {wl.n_maps} maps ({wl.name}), {n_steps} float64 DDIM steps + LAPACK MDS, "
                       f"one thread; {ts:.1f} s sampling + {tm:.1f} s MDS",
             "mds_maps_per_s": n_maps / tm, "step_traj_steps_per_s": n_maps * n_steps / ts,
             "host_cpu_count": os.cpu_count(), "host_affinity": len(os.sched_getaffinity(0)),
-            "host_cpu_model": cpu_model()}
+            "host_cpu_model": cpu_model(), "sample_maps": n_maps}
+
+
+def cpu_baseline_parallel(wl, n_steps, seed, per_worker_maps, procs):
+    """The same oracle in `procs` processes (one BLAS thread each) over disjoint blocks of
+    the workload, per_worker_maps maps per process where the workload holds that many:
+    the best figure the host's cores reach without changing the oracle."""
+    import multiprocessing as mp
+
+    L = wl.chain_len
+    units = wl.n_maps if L == 1 else wl.n_guidance * wl.n_traj    # maps, or joint-sample columns
+    per = per_worker_maps if L == 1 else max(1, per_worker_maps // L)
+    total = min(units, per * procs)
+    bounds = [total * j // procs for j in range(procs + 1)]
+    blocks = [(wl.name, n_steps, seed, bounds[j], bounds[j + 1] - bounds[j])
+              for j in range(procs) if bounds[j + 1] > bounds[j]]
+    with mp.get_context("fork").Pool(len(blocks)) as pool:
+        t0 = time.perf_counter()
+        res = pool.map(_oracle_block_star, blocks, chunksize=1)
+        wall = time.perf_counter() - t0
+    maps = sum(r[0] for r in res)
+    return {"value": maps * n_steps / wall, "unit": "trajectory-steps/s", "cores": len(blocks),
+            "kind": "oracle, one process per core",
+            "sample": f"{maps} of {wl.n_maps} maps ({wl.name}) in {len(blocks)} blocks, {n_steps} float64 DDIM "
+                      f"steps + LAPACK MDS; {wall:.1f} s wall"}
 
 
 def cpu_model() -> str:
@@ -375,8 +410,12 @@ def main():
         return copy_only(args, wl)
     n_steps = args.n_steps or wl.n_steps[0]
     if args.cpu_only:
-        print(json.dumps({"workload": wl.name, "ddim_steps": n_steps,
-                          "cpu_baseline": cpu_baseline(wl, n_steps, args.seed, args.cpu_seconds)}), flush=True)
+        out = {"workload": wl.name, "ddim_steps": n_steps,
+               "cpu_baseline": cpu_baseline(wl, n_steps, args.seed, args.cpu_seconds)}
+        if args.cpu_procs > 0:
+            out["cpu_baseline_parallel"] = cpu_baseline_parallel(
+                wl, n_steps, args.seed, out["cpu_baseline"]["sample_maps"], args.cpu_procs)
+        print(json.dumps(out), flush=True)
         return None
     if args.sync_ablation:
         return sync_ablation(args, wl, n_steps)
