@@ -125,6 +125,18 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t n) {
     return x * per + (x < rem ? x : rem) + i;
 }
 
+// Chunked variant: XCD x works through chunks x, x + 8, x + 16, ... of C
+// consecutive logical workgroups, so the eight XCDs stream neighbouring
+// address ranges at any moment.  Workgroups past the last whole round of
+// 8 C keep their order.  A bijection on [0, n).
+__device__ __forceinline__ uint32_t xcd_remap_chunked(uint32_t b, uint32_t n, uint32_t C) {
+    constexpr uint32_t kXcd = 8;
+    const uint32_t full = n / (kXcd * C) * (kXcd * C);
+    if (b >= full) return b;
+    const uint32_t x = b % kXcd, i = b / kXcd;
+    return ((i / C) * kXcd + x) * C + i % C;
+}
+
 // Wavefront sum by DPP: quad permutes, then the half-row and row mirrors
 // leave every lane of a 16-lane row holding the row total (each step adds a
 // value to its mirror image, so the lanes of a row round identically); row
