@@ -76,6 +76,7 @@ def test_whole_loop_entry_point_matches_step_loop():
     (2, 3, 9, (0.0, 1.0, 2.5), 0.5, 20),  # three weights, eta between DDIM and DDPM
     (2, 2, 5, (0.0, 1.0), 1.0, 1000),     # stride-1 DDPM-equivalent chain
     (2, 16, 3, tuple(0.2 * g for g in range(16)), 1.0, 50),  # the most guidance weights a layout takes
+    (13, 2, 100, (0.0, 1.0), 1.0, 10),    # 1300 workgroups: two whole rounds of XCD chunks and a tail
 ])
 def test_edge_layouts(R, G, S, w, eta, n_steps):
     wl = Workload("edge", "", R, G, S, 1, 0, 0, (n_steps,), eta, w, None, 9)
