@@ -41,7 +41,8 @@ __device__ __forceinline__ float start_vec(int i, int k) { return kMdsStart[i][k
 
 // Cyclic Jacobi on a symmetric 4x4 (values identical in every lane).  The
 // rotation that zeroes h_pq uses t = sgn(th) / (|th| + sqrt(th^2 + 1)) with
-// th = (h_qq - h_pp) / (2 h_pq), c = 1 / sqrt(1 + t^2), s = t c; only the
+// th = (h_qq - h_pp) / (2 h_pq) (formed as 2 h_pq sgn(d) / (|d| + sqrt(d^2 +
+// 4 h_pq^2)), d = h_qq - h_pp), c = 1 / sqrt(1 + t^2), s = t c; only the
 // entries it changes are updated (h_pp -= t h_pq, h_qq += t h_pq, rows r != p,
 // q rotate).  t needs no correct rounding: c and s are formed from it, so the
 // rotation stays orthogonal, and the hardware rcp / rsq / sqrt are used.  The
@@ -53,10 +54,11 @@ template <int P, int Q>
 __device__ __forceinline__ void jacobi_rotate(float (&h)[kBlk][kBlk], float (&wl)[kBlk], float skip2) {
     const float apq = h[P][Q];
     if (apq * apq <= skip2) return;  // wave-uniform
-    const float th = (h[Q][Q] - h[P][P]) * 0.5f * __builtin_amdgcn_rcpf(apq);
-    const float at = fabsf(th);
-    const float t = at > 1e18f ? 0.5f * __builtin_amdgcn_rcpf(th)
-                               : copysignf(__builtin_amdgcn_rcpf(at + __builtin_amdgcn_sqrtf(fmaf(th, th, 1.f))), th);
+    // t = sgn(th) / (|th| + sqrt(th^2 + 1)) with th = d / (2 h_pq), d = h_qq - h_pp,
+    // multiplied through by 2 |h_pq|: one transcendental fewer, and no overflow of th
+    const float d = h[Q][Q] - h[P][P];
+    const float den = fabsf(d) + __builtin_amdgcn_sqrtf(fmaf(d, d, 4.f * apq * apq));
+    const float t = copysignf(2.f, d) * apq * __builtin_amdgcn_rcpf(den);
     const float c = __builtin_amdgcn_rsqf(fmaf(t, t, 1.f));
     const float sn = t * c;
     h[P][P] = fmaf(-t, apq, h[P][P]);
