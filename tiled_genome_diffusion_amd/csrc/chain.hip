@@ -63,17 +63,27 @@ __global__ __launch_bounds__(kThreads) void k_step_chain(float *__restrict__ sta
 
     // Seam membership of this lane's four elements (pair index or -1), and
     // whether its 128-byte line (elements 32 m .. 32 m + 31) holds a
-    // left-seam element.  A line spans at most two rows of the map.
-    int lp[4], rp[4];
-#pragma unroll
-    for (int l = 0; l < 4; ++l) {
-        int i = 0, j = 1;
-        if (active) packed_row_col(static_cast<int>(4 * q) + l, i, j);
-        lp[l] = (active && j < O) ? block_pair_index(i, j, O) : -1;
-        rp[l] = (active && i >= off) ? block_pair_index(i - off, j - off, O) : -1;
-    }
+    // left-seam element.  A line spans at most two rows of the map.  Only
+    // wavefronts whose 256 elements reach a seam row work it out (rows
+    // 0..O-2 hold the left seam, rows 64-O.. the right one): it costs as
+    // much VALU as stepping a map, and most wavefronts hold no seam element.
+    int lp[4] = {-1, -1, -1, -1}, rp[4] = {-1, -1, -1, -1};
     bool seam_line = false;
-    if (active) {
+    const int wave_e0 = __builtin_amdgcn_readfirstlane(static_cast<int>(q >> 6)) * 256;
+    const bool may_left = wave_e0 <= packed_index(O - 2, O - 1);
+    const bool may_right = wave_e0 + 255 >= packed_index(off, off + 1);
+    if (active && (may_left || may_right)) {
+        int i = 0, j = 1;
+        packed_row_col(static_cast<int>(4 * q), i, j);
+#pragma unroll
+        for (int l = 0; l < 4; ++l) {
+            if (l > 0 && ++j == kBeads) {  // next element: next column, or the next row's first
+                ++i;
+                j = i + 1;
+            }
+            lp[l] = j < O ? block_pair_index(i, j, O) : -1;
+            rp[l] = i >= off ? block_pair_index(i - off, j - off, O) : -1;
+        }
         const int e0 = static_cast<int>(q / 8) * 32, e1 = e0 + 31;
         int i0, j0, i1, j1;
         packed_row_col(e0, i0, j0);

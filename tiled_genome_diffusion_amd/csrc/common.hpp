@@ -21,10 +21,11 @@ __host__ __device__ constexpr int packed_index(int i, int j) {
 
 // Row and column of packed element e (inverse of packed_index).  Row i starts
 // at i (2n - i - 1) / 2, so i is the floor of the smaller root of that
-// quadratic; a float estimate is corrected by at most one step each way.
-__host__ __device__ inline void packed_row_col(int e, int &i, int &j) {
+// quadratic; a float estimate (the hardware square root, within a few ulp of
+// a root below 128) is corrected by at most one step each way.
+__device__ inline void packed_row_col(int e, int &i, int &j) {
     constexpr int b = 2 * kBeads - 1;
-    int r = static_cast<int>((b - sqrtf(static_cast<float>(b * b - 8 * e))) * 0.5f);
+    int r = static_cast<int>((b - __builtin_amdgcn_sqrtf(static_cast<float>(b * b - 8 * e))) * 0.5f);
     r = r < 0 ? 0 : (r > kBeads - 2 ? kBeads - 2 : r);
     if (r < kBeads - 2 && packed_index(r + 1, r + 2) <= e) ++r;
     if (r > 0 && packed_index(r, r + 1) > e) --r;
