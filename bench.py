@@ -35,7 +35,9 @@ def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=6, help="timed passes")
-    p.add_argument("--warmup", type=int, default=1, help="untimed passes")
+    p.add_argument("--warmup", type=int, default=None,
+                   help="untimed passes (default: 1 for states of 1 GB and more, else 30: passes of a few "
+                        "milliseconds do not settle the GPU's clocks)")
     p.add_argument("--workload", default="genome_slab")
     p.add_argument("--n-steps", type=int, default=0, help="DDIM steps (default: the workload's first)")
     p.add_argument("--seed", type=int, default=0, help="seed of the ablation and cpu baseline")
@@ -404,6 +406,8 @@ def main():
     from workloads import get, reference_maps
 
     wl = get(args.workload)
+    if args.warmup is None:
+        args.warmup = 1 if wl.n_maps * 2016 * 4 >= 1 << 30 else 30
     if args.traffic_summary:
         return traffic_summary(args, wl)
     if args.copy_only:
