@@ -63,17 +63,19 @@ def parse():
     p.add_argument("--traffic-summary", default="", metavar="PMC_DIR",
                    help="no GPU: turn the FETCH_SIZE / WRITE_SIZE counter runs under PMC_DIR (copy_<C>/ and "
                         "slab_<C>/ rocprofv3 csv output) into profiles/k_step_indep_<workload>_traffic.json")
+    p.add_argument("--traffic-out", default="", metavar="PATH",
+                   help="with --traffic-summary: write the JSON here instead of under profiles/")
     p.add_argument("--copy-only", action="store_true",
                    help="time a plain device-to-device copy of the workload's state size instead "
                         "(the calibration kernel for the HBM byte counters)")
     return p.parse_args()
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, directory: str = os.path.join(ROOT, "profiles")):
     """HBM bytes per step launch from the committed FETCH_SIZE/WRITE_SIZE counter runs
     (profiles/*_traffic.json), or None if none matches this workload or the kernel
     source has changed since the counters were taken."""
-    for path in glob.glob(os.path.join(ROOT, "profiles", "*_traffic.json")):
+    for path in glob.glob(os.path.join(directory, "*_traffic.json")):
         with open(path) as f:
             d = json.load(f)
         if d.get("workload") != workload:
@@ -134,7 +136,8 @@ def traffic_summary(args, wl):
            "traffic_bytes_per_launch": rd + wr, "fetch_bytes_per_launch": rd, "write_bytes_per_launch": wr,
            "algorithmic_read_bytes": wl.n_maps * 2016 * 4 + wl.n_regions * REF_BYTES_PER_REGION,
            "algorithmic_write_bytes": wl.n_maps * 2016 * 4}
-    with open(os.path.join(ROOT, "profiles", f"k_step_indep_{wl.name}_traffic.json"), "w") as f:
+    dest = args.traffic_out or os.path.join(ROOT, "profiles", f"k_step_indep_{wl.name}_traffic.json")
+    with open(dest, "w") as f:
         json.dump(out, f, indent=1)
     for k in sorted(fetch):
         fr, wr_ = fetch[k][0], write.get(k, (float("nan"), 0))[0]
