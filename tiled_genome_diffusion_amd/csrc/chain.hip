@@ -7,10 +7,10 @@ namespace {
 
 constexpr int kChainU = 1;           // maps per lane per barrier, chain layout (measured best on MI355X)
 // Maps of one (tile, weight) per workgroup, chain layout: enough to amortise
-// the per-workgroup set-up and barriers, while keeping about kChainGrid
-// workgroups in the grid (measured best on MI355X: 8 for 16,384 maps, 16 for
-// 32,000).
-constexpr int kChainMapsMin = 4, kChainMapsMax = 16, kChainGrid = 2048;
+// the per-workgroup set-up and barriers.  Measured on MI355X with settled
+// clocks: 6 is best for both the 16,384-map and the 32,000-map chain (41.8 and
+// 76.2 us per step; 8 maps: 41.8 and 78.8; 4: 44 and 80; 10: 44.8 and 80.6).
+constexpr int kChainMaps = 6;
 
 // Workgroups are laid out as for independent maps: one workgroup
 // steps a.maps_per_block maps of one tile k (region r = c L + k) and weight g.
@@ -193,9 +193,7 @@ hipError_t launch_step_chain(float *state, const float *x0c, const float *x0u, c
                              StepArgs a, ChainArgs ch, bool project, float *pre_disc, bool noise, bool init,
                              hipStream_t stream) {
     const int64_t n_maps = static_cast<int64_t>(a.R) * a.G * a.S;
-    int64_t mpb = (n_maps / kChainGrid) & ~int64_t(1);
-    mpb = mpb < kChainMapsMin ? kChainMapsMin : (mpb > kChainMapsMax ? kChainMapsMax : mpb);
-    a.maps_per_block = static_cast<int32_t>(mpb);
+    a.maps_per_block = kChainMaps;
     a.blocks_per_rg = (a.S + a.maps_per_block - 1) / a.maps_per_block;
     const int64_t blocks = static_cast<int64_t>(a.R) * a.G * a.blocks_per_rg;
     const dim3 grid(static_cast<uint32_t>(blocks));
