@@ -212,8 +212,8 @@ PC_API pc_status pc_seam_discrepancy(const float *state, const pc_layout *layout
  * Seam discrepancy in the paper's form (section 5.5, Eq. (6); the equation
  * itself was lost, read from its description): per seam and guidance weight,
  * the mean over the shared pairs of |mean_s left copy - mean_s right copy|,
- * the sample means taken over the S trajectories.  Sums run in float64 in
- * trajectory order; deterministic.
+ * the sample means taken over the S trajectories.  Sums run in float64 in a
+ * fixed order, so the result is deterministic.
  *   out  device float [n_chains*(chain_len-1)][G], written.
  * Errors: NULL pointers; bad layout; chain_len < 2.
  */
