@@ -143,7 +143,9 @@ __device__ __forceinline__ uint32_t xcd_remap_chunked(uint32_t b, uint32_t n, ui
 // value to its mirror image, so the lanes of a row round identically); row
 // broadcasts 15 and 31 fold the four rows into lane 63, which is read back
 // as a wave-uniform value.  Six full-rate DPP adds and one readlane, in a
-// fixed order.
+// fixed order.  Only lane 63 is read, so the broadcasts run on every row
+// (rows 0-2 end with partial sums nobody reads): with full row masks each
+// folds into a single v_add_f32_dpp.
 template <int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ float dpp(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
@@ -153,9 +155,30 @@ __device__ __forceinline__ float wave_sum(float v) {
     v += dpp<0x4E>(v);         // quad_perm [2,3,0,1]
     v += dpp<0x141>(v);        // row_half_mirror
     v += dpp<0x140>(v);        // row_mirror
-    v += dpp<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
-    v += dpp<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+    v += dpp<0x142>(v);        // row_bcast:15: row r += row r - 1 (rows 1 and 3 matter)
+    v += dpp<0x143>(v);        // row_bcast:31: rows 2 and 3 += row 1
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// N independent wavefront sums, stage by stage: each value takes exactly the
+// steps of wave_sum (same bits), and the DPP adds of different values fill
+// each other's wait states instead of leaving one dependent chain to stall.
+template <int N>
+__device__ __forceinline__ void wave_sums(float (&v)[N]) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) v[n] += dpp<0xB1>(v[n]);
+#pragma unroll
+    for (int n = 0; n < N; ++n) v[n] += dpp<0x4E>(v[n]);
+#pragma unroll
+    for (int n = 0; n < N; ++n) v[n] += dpp<0x141>(v[n]);
+#pragma unroll
+    for (int n = 0; n < N; ++n) v[n] += dpp<0x140>(v[n]);
+#pragma unroll
+    for (int n = 0; n < N; ++n) v[n] += dpp<0x142>(v[n]);
+#pragma unroll
+    for (int n = 0; n < N; ++n) v[n] += dpp<0x143>(v[n]);
+#pragma unroll
+    for (int n = 0; n < N; ++n) v[n] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[n]), 63));
 }
 
 // Coefficients of one guided DDIM step, rounded to float32 from float64 on

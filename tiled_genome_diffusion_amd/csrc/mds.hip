@@ -1,9 +1,10 @@
 // Batched classical (Torgerson) MDS: one 64-lane workgroup per map, lane i
 // owning bead i.
 //
-//   1. The packed map is staged in LDS (504 coalesced float4 loads); lane i
+//   1. The packed map is copied from HBM straight into LDS (global_load_lds,
+//      eight 16-byte loads per lane that bypass the registers); lane i
 //      gathers row i of A = D o D into 64 VGPRs (two constant-offset LDS
-//      reads and a select per entry).
+//      reads and a select on a constant lane mask per entry).
 //   2. Double centring B = J A J (times -1/2) from the row means (LDS) and the
 //      grand mean (wavefront reduction); row i of B stays in VGPRs.
 //   3. Block-4 subspace iteration with Rayleigh-Ritz: Q <- orth(Z) by
@@ -49,7 +50,9 @@ __device__ __forceinline__ float start_vec(int i, int k) { return kMdsStart[i][k
 // eigenvector matrix W is spread over lanes: lane r < 4 holds row r in wl, so
 // a rotation costs each lane two columns of one row.  Rotations whose h_pq^2
 // is below `skip2` (1e-15 of the squared diagonal norm, under float32
-// resolution of the largest eigenvalue) are skipped.
+// resolution of the largest eigenvalue) are skipped.  (Carrying skipped
+// rotations out as identities with selects instead of a branch measured 4%
+// slower over the whole kernel.)
 template <int P, int Q>
 __device__ __forceinline__ void jacobi_rotate(float (&h)[kBlk][kBlk], float (&wl)[kBlk], float skip2) {
     const float apq = h[P][Q];
@@ -102,14 +105,29 @@ __device__ __forceinline__ void jacobi4(float (&h)[kBlk][kBlk], float (&wl)[kBlk
     }
 }
 
+// hi in lanes above lane j (lane id > j), lo in lanes 0 .. j, for a wavefront
+// with all 64 lanes active.  The lane mask is the execution mask shifted by
+// j + 1 (one scalar shift once the caller's loop over j is unrolled), and the
+// select a single v_cndmask on that SGPR pair, with no vector compare.  (The
+// mask is not written as a 64-bit constant: hipcc encodes such a constant as
+// a 32-bit literal that gfx950 zero-extends, which loses the upper 32 lanes;
+// measured.  The asm is one ALU instruction on ordinary registers, so the
+// compiler places every wait before it.)
+__device__ __forceinline__ float select_above(float lo, float hi, int j) {
+    const uint64_t above = j < kLanes - 1 ? __builtin_amdgcn_read_exec() << (j + 1) : 0ull;
+    float r;
+    asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(lo), "v"(hi), "s"(above));
+    return r;
+}
+
 // Largest value over the wavefront of a non-negative v (DPP, as wave_sum).
 __device__ __forceinline__ float wave_max_nonneg(float v) {
     v = fmaxf(v, dpp<0xB1>(v));
     v = fmaxf(v, dpp<0x4E>(v));
     v = fmaxf(v, dpp<0x141>(v));
     v = fmaxf(v, dpp<0x140>(v));
-    v = fmaxf(v, dpp<0x142, 0xA>(v));
-    v = fmaxf(v, dpp<0x143, 0xC>(v));
+    v = fmaxf(v, dpp<0x142>(v));  // only lane 63 is read (as in wave_sum)
+    v = fmaxf(v, dpp<0x143>(v));
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
@@ -117,7 +135,10 @@ __device__ __forceinline__ float wave_max_nonneg(float v) {
 // loses more than 4 decimal digits of its norm to the projections (the fourth
 // column of B Q when B has rank 3) is projected a second time, which restores
 // orthogonality to float32 precision; a column that vanishes is replaced by
-// its start vector.
+// its start vector.  (Classical Gram-Schmidt, whose coefficients come from one
+// batch of sums, measured 5% slower over the whole kernel: it issues more
+// instructions, and the kernel is bound by instruction issue, not by the
+// latency of the reductions.)
 __device__ __forceinline__ void orthonormalise(int lane, const float (&y)[kBlk], float (&q)[kBlk]) {
 #pragma unroll
     for (int k = 0; k < kBlk; ++k) {
@@ -241,15 +262,24 @@ __device__ __forceinline__ void subspace(const float (&b)[kBeads], float diag_er
         block_matvec(b, diag_err, lane, q, s_q, z);
         project_out(dfl, lane, z);
         if (it == 0) continue;  // the first product only seeds the subspace
-        float h[kBlk][kBlk], wl[kBlk];
+        float h[kBlk][kBlk], wl[kBlk], hs[kBlk * (kBlk + 1) / 2];
+        {
+            int n = 0;
 #pragma unroll
-        for (int r = 0; r < kBlk; ++r)
+            for (int r = 0; r < kBlk; ++r)
 #pragma unroll
-            for (int c = r; c < kBlk; ++c) {
-                const float sm = wave_sum(fmaf(q[r], z[c], q[c] * z[r])) * 0.5f;
-                h[r][c] = sm;
-                h[c][r] = sm;
-            }
+                for (int c = r; c < kBlk; ++c) hs[n++] = fmaf(q[r], z[c], q[c] * z[r]);
+            wave_sums(hs);
+            n = 0;
+#pragma unroll
+            for (int r = 0; r < kBlk; ++r)
+#pragma unroll
+                for (int c = r; c < kBlk; ++c) {
+                    const float sm = hs[n++] * 0.5f;
+                    h[r][c] = sm;
+                    h[c][r] = sm;
+                }
+        }
         jacobi4(h, wl, lane);
         float d[kBlk] = {h[0][0], h[1][1], h[2][2], h[3][3]};
         // Sort descending, carrying the eigenvector columns (selects only).
@@ -290,12 +320,18 @@ __device__ __forceinline__ void subspace(const float (&b)[kBeads], float diag_er
         // to deflate take 4e-6.
         const bool hide = may_hide(d, rho);
         const float cap = 4e-6f * thmax, floor_tol = 5e-7f * thmax;
+        float r2s[kBlk];  // squared residual norms, all four in one batch of sums
+#pragma unroll
+        for (int k = 0; k < kBlk; ++k) {
+            const float r = fmaf(-d[k], vec[k], yv[k]);
+            r2s[k] = r * r;
+        }
+        wave_sums(r2s);
         bool done = true;
 #pragma unroll
         for (int k = 0; k < kBlk; ++k) {
             if (!done || (!hide && k == 3)) break;  // wave-uniform
-            const float r = fmaf(-d[k], vec[k], yv[k]);
-            const float r2 = wave_sum(r * r);
+            const float r2 = r2s[k];
             float tk = cap;
             if (!hide && d[k] > 0.f) {
                 float g = k == 2 ? d[k] - rho : 3.4e38f;
@@ -329,6 +365,26 @@ __device__ __forceinline__ void subspace(const float (&b)[kBeads], float diag_er
     }
 }
 
+// Copies packed map m from HBM straight into LDS with global_load_lds (each
+// instruction writes lane l's 16 bytes at s_map + 16 l), without passing
+// through registers.  Asynchronous: the compiler waits for it before the
+// first LDS read of s_map.
+__device__ __forceinline__ void stage_map(const float *maps, size_t m, float4 *s_map, int lane) {
+    typedef __attribute__((address_space(1))) void *gptr;
+    typedef __attribute__((address_space(3))) void *lptr;
+    const char *src = reinterpret_cast<const char *>(maps + m * kPacked);  // wave-uniform
+    const uint32_t off = static_cast<uint32_t>(lane) * 16u;                 // the lane's bytes in a chunk
+#pragma unroll
+    for (int c = 0; c < kQuads / kLanes; ++c)
+        __builtin_amdgcn_global_load_lds((gptr)(src + c * kLanes * 16 + off), (lptr)(s_map + c * kLanes), 16, 0, 0);
+    constexpr int kTail = kQuads % kLanes;  // 56 quads in the last chunk
+    if (lane < kTail) {
+        constexpr int c = kQuads / kLanes;
+        __builtin_amdgcn_global_load_lds((gptr)(src + c * kLanes * 16 + off), (lptr)(s_map + c * kLanes), 16, 0, 0);
+    }
+}
+
+// One map per 64-lane workgroup, lane i owning bead i.
 __global__ __launch_bounds__(kLanes, 4) void k_mds(const float *__restrict__ maps, float *__restrict__ coords,
                                                 float *__restrict__ eigvals, int32_t max_iters) {
     __shared__ float4 s_map[kQuads];
@@ -336,9 +392,7 @@ __global__ __launch_bounds__(kLanes, 4) void k_mds(const float *__restrict__ map
     __shared__ __align__(16) float s_mean[kBeads];
     const int i = threadIdx.x;
     const size_t m = blockIdx.x;
-
-    const float4 *src = reinterpret_cast<const float4 *>(maps + m * kPacked);
-    for (int k = i; k < kQuads; k += kLanes) s_map[k] = src[k];
+    stage_map(maps, m, s_map, i);
     __syncthreads();
     const float *xs = reinterpret_cast<const float *>(s_map);
 
@@ -362,7 +416,7 @@ __global__ __launch_bounds__(kLanes, 4) void k_mds(const float *__restrict__ map
         } else {
             const float dr = row[j - 1];
             const float dc = col[packed_index(j, j + 1) - j - 1];
-            d = j < i ? dc : dr;
+            d = select_above(dr, dc, j);  // j < i ? dc : dr
         }
         b[j] = d * d;
         rsum += b[j];
