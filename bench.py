@@ -29,6 +29,12 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 STEP_BYTES_PER_MAP = 2016 * 4 * 2   # read + write of one packed map per DDIM step
 REF_BYTES_PER_REGION = 2016 * 4 * 2  # conditional + unconditional reference, once per region per step
+FP32_PEAK_TFLOPS = 157.3       # MI355X FP32 vector, published
+# Algorithmic flops of classical MDS on one map along the path a Euclidean map takes (two
+# products B Q and one Rayleigh-Ritz step): squaring and double centring 16,384; the two
+# 64x64x4 products 65,536; Gram-Schmidt of four columns 2,304; H = Q^T Z 1,280; Ritz vectors
+# and residuals 4,864; output 192.
+MDS_FLOPS_PER_MAP = 16384 + 65536 + 2304 + 1280 + 4864 + 192
 
 
 def parse():
@@ -588,6 +594,10 @@ def main():
         "step_loop_traj_steps_per_s": traj_steps / (step_ms * 1e-3),
         "mds_maps_per_s": lay.n_maps / (mds_ms * 1e-3),
         "mds_ms": mds_ms,
+        "mds_roofline": {"bound": "alu", "kernel": "k_mds", "unit": "TFLOP/s", "peak": FP32_PEAK_TFLOPS,
+                         "achieved": MDS_FLOPS_PER_MAP * lay.n_maps / (mds_ms * 1e-3) / 1e12,
+                         "frac": MDS_FLOPS_PER_MAP * lay.n_maps / (mds_ms * 1e-3) / 1e12 / FP32_PEAK_TFLOPS,
+                         "flops_per_map": MDS_FLOPS_PER_MAP},
         "step_loop_ms": step_ms,
     }
     if not args.no_cpu_baseline:
