@@ -139,3 +139,20 @@ def test_noise_maps_stay_finite_and_ordered():
     assert np.all(np.isfinite(coords)) and np.all(np.isfinite(eig))
     assert np.all(eig[:, 0] >= eig[:, 1]) and np.all(eig[:, 1] >= eig[:, 2])
     assert np.array_equal(coords, coords2) and np.array_equal(eig, eig2)
+
+
+def test_batch_slices_match_the_whole_batch():
+    # one map, and batches that start inside a larger allocation (the maps are copied into
+    # LDS by 16-byte lanes from any 16-byte aligned start): bitwise the rows of the whole run
+    torch, dev = torch_dev()
+    say("mds on slices of a batch")
+    walks = [random_walk(64, walk_rng(21, k), 0.25) for k in range(13)]
+    maps = torch.from_numpy(np.array([packed_distances(w) for w in walks], dtype=np.float32)).to(dev)
+    n = maps.shape[0]
+    whole = torch.empty(n * 64 * 3, dtype=torch.float32, device=dev)
+    pc.pc_mds_recover(maps, whole)
+    whole = whole.view(n, 64, 3)
+    for lo, hi in ((0, 1), (12, 13), (5, 6), (3, 10), (1, 13)):
+        out = torch.empty((hi - lo) * 64 * 3, dtype=torch.float32, device=dev)
+        pc.pc_mds_recover(maps[lo:hi], out)
+        assert torch.equal(out.view(hi - lo, 64, 3), whole[lo:hi])
