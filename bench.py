@@ -29,7 +29,11 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 STEP_BYTES_PER_MAP = 2016 * 4 * 2   # read + write of one packed map per DDIM step
 REF_BYTES_PER_REGION = 2016 * 4 * 2  # conditional + unconditional reference, once per region per step
-FP32_PEAK_TFLOPS = 157.3       # MI355X FP32 vector, published
+FP32_PEAK_TFLOPS = 157.3       # MI355X FP32 vector, published (counts packed-FP32 instructions)
+# Non-packed FP32 vector peak: 256 CUs x 4 SIMDs x 16 lanes x 2 flops (FMA) x 2.4 GHz.  The library
+# is built with packed-FP32 instructions disabled, so this is the ceiling its vector code can reach.
+FP32_NONPACKED_PEAK_TFLOPS = 78.6
+MDS_BYTES_PER_MAP = 2016 * 4 + 64 * 3 * 4   # packed map read + coordinates written (eigenvalues optional)
 # Algorithmic flops of classical MDS on one map along the path a Euclidean map takes (two
 # products B Q and one Rayleigh-Ritz step): squaring and double centring 16,384; the two
 # 64x64x4 products 65,536; Gram-Schmidt of four columns 2,304; H = Q^T Z 1,280; Ritz vectors
@@ -74,6 +78,16 @@ def parse():
     p.add_argument("--copy-only", action="store_true",
                    help="time a plain device-to-device copy of the workload's state size instead "
                         "(the calibration kernel for the HBM byte counters)")
+    p.add_argument("--ceilings", action="store_true",
+                   help="time the bandwidth probes (in-place read-modify-write, read-only and write-only "
+                        "streams with the step kernel's access pattern) and the x_T fill on the workload's state; "
+                        "one JSON line")
+    p.add_argument("--seam-report", action="store_true",
+                   help="on a chain workload: per-step seam discrepancy before projection (the fused "
+                        "discrepancy output of the step) and after it (pc_seam_discrepancy), against the "
+                        "closed-form expectation, and the step time with and without the discrepancy output")
+    p.add_argument("--jacobi-maps", type=int, default=8,
+                   help="maps the cpu baseline runs through the Jacobi MDS oracle (0.5 s each on one core)")
     return p.parse_args()
 
 
@@ -96,7 +110,8 @@ def measured_traffic(workload: str, directory: str = os.path.join(ROOT, "profile
 
 
 STEP_SOURCES = ["tiled_genome_diffusion_amd/csrc/step.hip", "tiled_genome_diffusion_amd/csrc/stream.hpp",
-                "tiled_genome_diffusion_amd/csrc/common.hpp"]
+                "tiled_genome_diffusion_amd/csrc/common.hpp", "tiled_genome_diffusion_amd/csrc/launch.hpp",
+                "tiled_genome_diffusion_amd/csrc/dispatch.hpp"]
 
 
 def traffic_summary(args, wl):
@@ -169,6 +184,151 @@ def copy_only(args, wl):
     dt = (time.perf_counter() - t0) / args.steps
     print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "ms": dt * 1e3,
                       "gbs": 2 * n * 4 / dt / 1e9, "workload": wl.name}), flush=True)
+
+
+def probe_lib():
+    """The bandwidth probes of libpc_ceiling.so (built beside libpc.so; not part of include/pc.h)."""
+    import ctypes
+
+    from tiled_genome_diffusion_amd import build as libbuild
+
+    if not os.path.exists(libbuild.CEILING_LIB):
+        raise SystemExit(f"{libbuild.CEILING_LIB} is not built (python -m tiled_genome_diffusion_amd.build)")
+    lib = ctypes.CDLL(libbuild.CEILING_LIB)
+    vp, i64, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float
+    lib.pcc_probe_rmw.argtypes = [vp, i64, f32, f32, vp]
+    lib.pcc_probe_read.argtypes = [vp, i64, f32, vp, vp]
+    lib.pcc_probe_write.argtypes = [vp, i64, f32, vp]
+    for f in (lib.pcc_probe_rmw, lib.pcc_probe_read, lib.pcc_probe_write):
+        f.restype = ctypes.c_int
+    return lib
+
+
+def hbm_probes(state, n_maps, stream, reps=5):
+    """GB/s of the three probes over `state` (n_maps packed maps; overwritten), each the median
+    of `reps` launches timed with HIP events on `stream`, after one untimed launch."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    lib = probe_lib()
+    ptr, st = ctypes.c_void_p(state.data_ptr()), ctypes.c_void_p(stream.cuda_stream)
+    sink = torch.zeros(1, dtype=torch.float32, device=state.device)
+    sink_p = ctypes.c_void_p(sink.data_ptr())
+    nbytes = n_maps * 2016 * 4
+    calls = {"rmw": (lambda: lib.pcc_probe_rmw(ptr, n_maps, 1.0, 0.0, st), 2 * nbytes),
+             "read": (lambda: lib.pcc_probe_read(ptr, n_maps, float("nan"), sink_p, st), nbytes),
+             "write": (lambda: lib.pcc_probe_write(ptr, n_maps, 0.5, st), nbytes)}
+    out = {}
+    for name, (fn, moved) in calls.items():
+        if fn() != 0:
+            raise RuntimeError(f"probe {name} failed to launch")
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e-3)
+        out[name + "_gbs"] = moved / float(np.median(times)) / 1e9
+    return out
+
+
+def ceilings(args, wl):
+    """The probes and the x_T fill (pc_init_state: write-only, non-temporal) on the workload's state."""
+    import numpy as np
+    import torch
+
+    import tiled_genome_diffusion_amd as pc
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    lay = pc.PCLayout(wl.n_regions, wl.n_guidance, wl.n_traj, wl.chain_len, wl.overlap if wl.chain_len > 1 else 0)
+    state = torch.empty(lay.n_maps * pc.PACKED, dtype=torch.float32, device=dev)
+    runs = []
+    for _ in range(max(1, args.steps)):
+        pc.pc_init_state(state, lay, args.seed)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        pc.pc_init_state(state, lay, args.seed)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        fill_gbs = lay.n_maps * 2016 * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        runs.append(dict(hbm_probes(state, lay.n_maps, stream), fill_gbs=fill_gbs))
+    med = {k: float(np.median([r[k] for r in runs])) for k in runs[0]}
+    print(json.dumps({"metric": "HBM ceilings, GB/s", "workload": wl.name, "state_bytes": lay.n_maps * 2016 * 4,
+                      "median": med, "runs": runs,
+                      "note": "rmw: in-place read-modify-write (bytes read + written); read / write: one "
+                              "stream; fill: pc_init_state (x_T, written)"}), flush=True)
+
+
+def seam_report(args, wl, n_steps):
+    """Seam discrepancy of a chain workload at every step: the RMS over the shared pairs per
+    (seam, weight, trajectory) before the projection (the fused output of the step kernel) and
+    after it (pc_seam_discrepancy), summarised as mean, mean square and max, beside the closed
+    form of the expected pre-projection mean square (2 sigma_i^2 from the second step on; the
+    first step compares independent draws of x_T).  Then the step time with and without the
+    fused discrepancy output, HIP events over whole 50-step loops."""
+    import numpy as np
+    import torch
+
+    import tiled_genome_diffusion_amd as pc
+    from workloads import reference_maps
+
+    if wl.chain_len < 2:
+        raise SystemExit("--seam-report needs a chain workload")
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    lay = pc.PCLayout(wl.n_regions, wl.n_guidance, wl.n_traj, wl.chain_len, wl.overlap)
+    x0c, x0u = reference_maps(wl, args.seed)
+    x0c_d, x0u_d = torch.from_numpy(x0c).to(dev), torch.from_numpy(x0u).to(dev)
+    state = torch.empty(lay.n_maps * pc.PACKED, dtype=torch.float32, device=dev)
+    n_cols = lay.n_seams * lay.n_guidance * lay.n_traj
+    pre = torch.empty(n_cols, dtype=torch.float32, device=dev)
+    rms = torch.empty(n_cols, dtype=torch.float32, device=dev)
+    summary = torch.empty(2, dtype=torch.float32, device=dev)
+    a_t, a_n = pc.pc_ddim_schedule(n_steps)
+    rows = []
+    pc.pc_init_state(state, lay, args.seed)
+    for i in range(n_steps):
+        pc.pc_ddim_cfg_step(state, x0c_d, x0u_d, list(wl.w), lay, a_t[i], a_n[i], wl.eta, args.seed, i + 1,
+                            project_seams=True, pre_disc=pre)
+        pc.pc_seam_discrepancy(state, lay, rms, summary)
+        p = pre.cpu().numpy().astype(np.float64)
+        q = rms.cpu().numpy().astype(np.float64)
+        a, an = a_t[i], a_n[i]
+        sig2 = wl.eta ** 2 * (1 - an) / (1 - a) * (1 - a / an)
+        expect = 2 * (1 - an - sig2) / (1 - a) + 2 * sig2 if i == 0 else 2 * sig2
+        rows.append({"step": i + 1, "pre_mean": float(p.mean()), "pre_mean_square": float((p * p).mean()),
+                     "pre_max": float(p.max()), "expected_pre_mean_square": expect,
+                     "post_mean": float(summary[0]), "post_max": float(summary[1]), "post_max_host": float(q.max())})
+
+    def loop(disc):
+        pc.pc_init_state(state, lay, args.seed)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n_steps):
+            pc.pc_ddim_cfg_step(state, x0c_d, x0u_d, list(wl.w), lay, a_t[i], a_n[i], wl.eta, args.seed, i + 1,
+                                project_seams=True, pre_disc=pre if disc else None)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n_steps
+
+    for _ in range(args.warmup):
+        loop(False)
+        loop(True)
+    times = {False: [], True: []}
+    for _ in range(max(1, args.steps)):   # interleaved, so clock drift hits both alike
+        times[False].append(loop(False))
+        times[True].append(loop(True))
+    print(json.dumps({"metric": "seam discrepancy before / after projection", "workload": wl.name,
+                      "ddim_steps": n_steps, "eta": wl.eta, "seams": lay.n_seams,
+                      "joint_samples": lay.n_guidance * lay.n_traj, "pairs_per_seam": wl.overlap * (wl.overlap - 1) // 2,
+                      "rows": rows,
+                      "step_us_projecting": float(np.median(times[False])),
+                      "step_us_projecting_with_discrepancy": float(np.median(times[True]))}), flush=True)
 
 
 def sync_ablation(args, wl, n_steps):
@@ -350,7 +510,28 @@ def _oracle_block_star(args):
     return _oracle_block(*args)
 
 
-def cpu_baseline(wl, n_steps, seed, target_s):
+def jacobi_mds_rate(wl, seed, n_maps):
+    """maps/s of the oracle's cyclic-Jacobi MDS (the brute-force eigensolver, one thread) on the
+    first n_maps reference maps of the workload (final states of the point-mass chain)."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import mds
+    from workloads import reference_maps
+
+    if n_maps <= 0:
+        return None
+    regions = list(range(min(wl.n_regions, (n_maps + 1) // 2))) if wl.chain_len == 1 else None
+    x0c, x0u = reference_maps(wl, seed, regions=regions)
+    maps = [m for pair in zip(x0c, x0u) for m in pair][:n_maps]
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for m in maps:
+            mds.classical_mds(m, solver="jacobi")
+        dt = time.perf_counter() - t0
+    return {"maps": len(maps), "seconds": dt, "maps_per_s": len(maps) / dt}
+
+
+def cpu_baseline(wl, n_steps, seed, target_s, jacobi_maps=0):
     """Time the oracle (as it stands) on a bounded sample of the workload, one thread."""
     L = wl.chain_len
     n = 16
@@ -362,6 +543,7 @@ def cpu_baseline(wl, n_steps, seed, target_s):
             "sample": f"{n_maps} of {wl.n_maps} maps ({wl.name}), {n_steps} float64 DDIM steps + LAPACK MDS, "
                       f"one thread; {ts:.1f} s sampling + {tm:.1f} s MDS",
             "mds_maps_per_s": n_maps / tm, "step_traj_steps_per_s": n_maps * n_steps / ts,
+            "jacobi_mds": jacobi_mds_rate(wl, seed, jacobi_maps),
             "host_cpu_count": os.cpu_count(), "host_affinity": len(os.sched_getaffinity(0)),
             "host_cpu_model": cpu_model(), "sample_maps": n_maps}
 
@@ -424,7 +606,7 @@ def main():
     n_steps = args.n_steps or wl.n_steps[0]
     if args.cpu_only:
         out = {"workload": wl.name, "ddim_steps": n_steps,
-               "cpu_baseline": cpu_baseline(wl, n_steps, args.seed, args.cpu_seconds)}
+               "cpu_baseline": cpu_baseline(wl, n_steps, args.seed, args.cpu_seconds, args.jacobi_maps)}
         if args.cpu_procs > 0:
             out["cpu_baseline_parallel"] = cpu_baseline_parallel(
                 wl, n_steps, args.seed, out["cpu_baseline"]["sample_maps"], args.cpu_procs)
@@ -434,6 +616,10 @@ def main():
         return sync_ablation(args, wl, n_steps)
     if args.chain_kernels:
         return chain_kernels(args, wl, n_steps)
+    if args.ceilings:
+        return ceilings(args, wl)
+    if args.seam_report:
+        return seam_report(args, wl, n_steps)
     dev = torch.device("cuda:0")
     lay = pc.PCLayout(wl.n_regions, wl.n_guidance, wl.n_traj, wl.chain_len, wl.overlap if wl.chain_len > 1 else 0)
     seeds = [int(v) for v in args.seeds.split(",")]
@@ -541,17 +727,9 @@ def main():
         per_seed.setdefault(seeds[k % len(seeds)], []).append(e[3].elapsed_time(e[2]))
     by_seed = {str(sd): traj_steps / (float(np.mean(v)) * 1e-3) for sd, v in per_seed.items()}
 
-    # the same bytes moved by a plain device-to-device copy (read + write of the state size)
-    dst = torch.empty_like(state)
-    dst.copy_(state)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record(stream)
-    for _ in range(5):
-        dst.copy_(state)
-    c1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbs = 2 * state.numel() * 4 / (c0.elapsed_time(c1) / 5 * 1e-3) / 1e9
-    del dst
+    # the ceiling of the step kernel's access pattern on this device: the in-place read-modify-write
+    # probe over the same state (which it overwrites; the passes are done with it)
+    probes = hbm_probes(state, lay.n_maps, stream)
 
     ms_per_pass = (t1 - t0) * 1e3 / args.steps
     step_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
@@ -588,20 +766,31 @@ def main():
                      "bytes_per_launch": loop_bytes / n_steps, "step_loop_bytes": loop_bytes,
                      # a launch that reads and writes the whole state: the basis of `traffic`
                      "bytes_per_steady_launch": bytes_per_launch,
-                     "copy_ceiling": copy_gbs, "frac_of_copy": achieved / copy_gbs},
+                     # measured live: the step's state access pattern with one FMA per element
+                     "ceiling": probes["rmw_gbs"], "frac_of_ceiling": achieved / probes["rmw_gbs"],
+                     "ceiling_kind": "in-place non-temporal float4 read-modify-write probe, step kernel's mapping",
+                     "read_ceiling": probes["read_gbs"], "write_ceiling": probes["write_gbs"]},
         "value_by_seed": by_seed,
         "value_sd_over_seeds": float(np.std(list(by_seed.values()), ddof=1)) if len(by_seed) > 1 else None,
         "step_loop_traj_steps_per_s": traj_steps / (step_ms * 1e-3),
         "mds_maps_per_s": lay.n_maps / (mds_ms * 1e-3),
         "mds_ms": mds_ms,
-        "mds_roofline": {"bound": "alu", "kernel": "k_mds", "unit": "TFLOP/s", "peak": FP32_PEAK_TFLOPS,
-                         "achieved": MDS_FLOPS_PER_MAP * lay.n_maps / (mds_ms * 1e-3) / 1e12,
-                         "frac": MDS_FLOPS_PER_MAP * lay.n_maps / (mds_ms * 1e-3) / 1e12 / FP32_PEAK_TFLOPS,
-                         "flops_per_map": MDS_FLOPS_PER_MAP},
+        # MDS moves 8,832 B and does about 90.6 k flops per map (10.3 flop/B).  Against 8 TB/s the bytes
+        # take 1.10 ns per map, the flops 1.15 ns at the non-packed FP32 peak (0.58 ns at the packed
+        # peak and on the matrix cores, which run two thirds of them): the two bounds meet, and the
+        # line reports the HBM one with the flop rate beside it
+        "mds_roofline": {"bound": "hbm", "kernel": "k_mds", "unit": "GB/s", "peak": HBM_PEAK_GBS,
+                         "achieved": MDS_BYTES_PER_MAP * lay.n_maps / (mds_ms * 1e-3) / 1e9,
+                         "frac": MDS_BYTES_PER_MAP * lay.n_maps / (mds_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "bytes_per_map": MDS_BYTES_PER_MAP, "flops_per_map": MDS_FLOPS_PER_MAP,
+                         "tflops": MDS_FLOPS_PER_MAP * lay.n_maps / (mds_ms * 1e-3) / 1e12,
+                         "frac_of_nonpacked_fp32": MDS_FLOPS_PER_MAP * lay.n_maps / (mds_ms * 1e-3) / 1e12
+                         / FP32_NONPACKED_PEAK_TFLOPS,
+                         "nonpacked_fp32_peak": FP32_NONPACKED_PEAK_TFLOPS},
         "step_loop_ms": step_ms,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, n_steps, args.seed, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(wl, n_steps, args.seed, args.cpu_seconds, args.jacobi_maps)
     print(json.dumps(out), flush=True)
 
 

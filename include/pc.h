@@ -30,7 +30,13 @@
  *         caller and must be 16-byte aligned; "host" arrays are host memory.
  *         The library allocates no device memory and keeps no state between
  *         calls (pc_ddim_sample holds its schedule in a host buffer for the
- *         length of the call); it is safe to call from several threads.
+ *         length of the call; the one setting, pc_set_max_dispatch_items, is
+ *         a diagnostic); it is safe to call from several threads.
+ * Sizes:  any layout with R G S <= 2^31 - 1 maps is accepted.  One dispatch
+ *         holds at most 2^32 - 1 work-items, so a kernel whose grid needs
+ *         more (e.g. the independent-map step beyond 16,777,214 maps, two
+ *         maps per 512-lane workgroup) is launched as consecutive slices of
+ *         the same grid on the same stream, with identical results.
  * Stream: `stream` is a hipStream_t (NULL = the null stream).  Device work is
  *         enqueued asynchronously on it; nothing synchronises.
  * Errors: argument errors are detected before any launch and return a
@@ -265,6 +271,16 @@ PC_API pc_status pc_kabsch_stitch(const float *coords, const pc_layout *layout, 
                                   void *stream);
 
 /* Diagnostics ----------------------------------------------------------- */
+
+/*
+ * Lowers the number of work-items any one kernel dispatch may hold (process
+ * wide; 0 restores the hardware's 2^32 - 1), so that tests can drive the
+ * sliced launches of large grids (see "Sizes" above) with small inputs.
+ * Results do not depend on it.  Not meant to change while other threads
+ * enqueue work.
+ * Errors: items outside 1024..2^32-1 (other than 0).
+ */
+PC_API pc_status pc_set_max_dispatch_items(uint64_t items);
 
 /* One Philox4x32-10 block on the host: out = Philox(ctr, key(seed)). */
 PC_API pc_status pc_philox_block(uint32_t out[4], const uint32_t ctr[4], uint64_t seed);

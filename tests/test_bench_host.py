@@ -78,11 +78,32 @@ def test_stored_traffic_is_used_only_while_the_source_is_unchanged(tmp_path):
 
 
 def test_cpu_only_reports_the_oracle_baseline_fields():
-    r = _run("--workload", "single_region", "--cpu-only", "--cpu-seconds", "0.2", "--cpu-procs", "2")
+    r = _run("--workload", "single_region", "--cpu-only", "--cpu-seconds", "0.2", "--cpu-procs", "2",
+             "--jacobi-maps", "2")
     assert r.returncode == 0, r.stderr
     d = json.loads(r.stdout.strip().splitlines()[-1])
     cb = d["cpu_baseline"]
     assert cb["value"] > 0 and cb["unit"] == "trajectory-steps/s" and cb["cores"] == 1 and cb["kind"] == "oracle"
     assert "16 of 16 maps" in cb["sample"]
+    assert cb["jacobi_mds"]["maps"] == 2 and cb["jacobi_mds"]["maps_per_s"] > 0
     par = d["cpu_baseline_parallel"]
     assert par["cores"] == 2 and par["value"] > 0
+
+
+def test_probe_library_exports_its_probes():
+    """The HBM-ceiling probes are built beside libpc.so, export their three entry points, and are
+    not part of include/pc.h."""
+    import re
+
+    from tiled_genome_diffusion_amd import build as libbuild
+
+    if not os.path.exists(libbuild.CEILING_LIB):
+        pytest.fail("libpc_ceiling.so is not built (python -m tiled_genome_diffusion_amd.build)")
+    out = subprocess.run(["nm", "-D", "--defined-only", libbuild.CEILING_LIB], capture_output=True, text=True,
+                         check=True).stdout
+    names = set(re.findall(r"\bT (pcc_\w+)", out))
+    assert names == {"pcc_probe_rmw", "pcc_probe_read", "pcc_probe_write"}
+    with open(os.path.join(ROOT, "include", "pc.h")) as f:
+        assert "pcc_" not in f.read()
+    bench = _bench_module()
+    assert bench.probe_lib() is not None

@@ -116,7 +116,7 @@ def test_projection_invariants_full_size():
     del noproj
 
 
-@pytest.mark.parametrize("n_steps", [50, 250, 1000])
+@pytest.mark.parametrize("n_steps", [50, 250, 500, 1000])
 def test_chr22_sweep_sampled_columns(n_steps):
     wl = get("chr22_sweep")
     cols = [(0, 0), (0, 999)]

@@ -17,7 +17,7 @@ from . import _lib
 
 __all__ = ["PCError", "PCLayout", "PACKED", "BEADS", "pc_version", "pc_last_error", "pc_ddim_schedule",
            "pc_ddim_schedule_cosine", "pc_init_state", "pc_ddim_cfg_step", "pc_ddim_cfg_step_eps", "pc_ddim_sample", "pc_seam_project", "pc_seam_discrepancy",
-           "pc_seam_mean_abs", "pc_mds_recover", "pc_kabsch_stitch", "pc_philox_block", "pc_philox_fill", "pc_normal_fill", "pc_seam_index_map"]
+           "pc_seam_mean_abs", "pc_mds_recover", "pc_kabsch_stitch", "pc_set_max_dispatch_items", "pc_philox_block", "pc_philox_fill", "pc_normal_fill", "pc_seam_index_map"]
 
 BEADS = 64
 PACKED = 2016
@@ -208,6 +208,11 @@ def pc_kabsch_stitch(coords, layout: PCLayout, chain, residual) -> None:
         _dev(chain, t.float32, n_chains * layout.n_guidance * layout.n_traj * n_beads * 3, "chain"),
         _dev(residual, t.float32, layout.n_seams * layout.n_guidance * layout.n_traj, "residual"),
         _stream(coords)), "pc_kabsch_stitch")
+
+
+def pc_set_max_dispatch_items(items: int) -> None:
+    """Cap the work-items of one kernel dispatch (0 restores the hardware limit); a diagnostic."""
+    _check(_lib.load().pc_set_max_dispatch_items(int(items)), "pc_set_max_dispatch_items")
 
 
 def pc_philox_block(ctr, seed: int):

@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <new>
 
 #include "pc.h"
@@ -47,7 +48,8 @@ pc_status check_layout(const pc_layout *L, int64_t *n_maps) {
     if (L->chain_len > 1 && (L->overlap < 2 || L->overlap > pc::kMaxOverlap))
         return fail(PC_ERR_SHAPE, "overlap %d outside 2..%d", L->overlap, pc::kMaxOverlap);
     const int64_t n = static_cast<int64_t>(L->n_regions) * L->n_guidance * L->n_traj;
-    // trajectory ids are 32-bit Philox counter words; grids are 32-bit
+    // trajectory ids are Philox counter words, kept below 2^31 for signed index
+    // arithmetic; grids beyond one dispatch's 2^32 - 1 work-items are launched in slices
     if (n > 0x7FFFFFFFLL) return fail(PC_ERR_SHAPE, "R*G*S = %lld exceeds 2^31 - 1", static_cast<long long>(n));
     if (L->chain_len > 1 && static_cast<int64_t>(L->n_guidance) * L->n_traj > 0x7FFFFFFFLL / L->chain_len)
         return fail(PC_ERR_SHAPE, "chain layout too large");
@@ -63,7 +65,12 @@ pc::ChainArgs chain_args(const pc_layout *L) {
     return ch;
 }
 
+// Work-items per dispatch; lowered only by the diagnostic pc_set_max_dispatch_items.
+std::atomic<uint64_t> g_dispatch_items{pc::kDispatchItemLimit};
+
 }  // namespace
+
+uint64_t pc::dispatch_items() { return g_dispatch_items.load(std::memory_order_relaxed); }
 
 extern "C" {
 
@@ -82,6 +89,14 @@ const char *pc_status_string(pc_status s) {
 }
 
 const char *pc_last_error(void) { return g_err; }
+
+pc_status pc_set_max_dispatch_items(uint64_t items) {
+    if (items == 0) items = pc::kDispatchItemLimit;
+    if (items < 1024 || items > pc::kDispatchItemLimit)
+        return fail(PC_ERR_PARAM, "dispatch cap %llu outside 1024..2^32-1", static_cast<unsigned long long>(items));
+    g_dispatch_items.store(items, std::memory_order_relaxed);
+    return ok();
+}
 
 pc_status pc_ddim_schedule(int32_t n_steps, int32_t T, double beta_start, double beta_end, double *abar_t,
                            double *abar_next) {

@@ -41,14 +41,14 @@ __global__ __launch_bounds__(kThreads) void k_step_chain(float *__restrict__ sta
                                                          const float *__restrict__ x0u,
                                                          const float *__restrict__ eps_c,
                                                          const float *__restrict__ eps_u, StepArgs a, ChainArgs ch,
-                                                         float *__restrict__ pre_disc) {
+                                                         float *__restrict__ pre_disc, int64_t block0) {
     static_assert(U <= kThreads - kQuads, "the discrepancy of map u is summed by idle lane kQuads + u");
     __shared__ float s_right[2][U][kMaxPairs];  // tile k's stepped right-seam values
     __shared__ float s_left[2][U][kMaxPairs];   // tile k+1's stepped left-seam values
 
     const uint32_t q = threadIdx.x;
     const bool active = q < kQuads;
-    const uint32_t b = xcd_remap(blockIdx.x, gridDim.x);
+    const uint32_t b = static_cast<uint32_t>(block0) + xcd_remap(blockIdx.x, gridDim.x);  // logical workgroup
     const int rg = static_cast<int>(b) / a.blocks_per_rg;
     const int chunk = static_cast<int>(b) - rg * a.blocks_per_rg;
     const int r = rg / a.G;
@@ -196,40 +196,41 @@ hipError_t launch_step_chain(float *state, const float *x0c, const float *x0u, c
     a.maps_per_block = kChainMaps;
     a.blocks_per_rg = (a.S + a.maps_per_block - 1) / a.maps_per_block;
     const int64_t blocks = static_cast<int64_t>(a.R) * a.G * a.blocks_per_rg;
-    const dim3 grid(static_cast<uint32_t>(blocks));
     const bool disc = pre_disc != nullptr;
     const bool nt = static_cast<size_t>(n_maps) * kPacked * 4 > kStreamBytes;
     const bool eps = eps_c != nullptr;
+    return launch_slices(blocks, kThreads, [&](int64_t first, uint32_t count) {
+        const dim3 grid(count);
 #define PC_CHAIN(P, D, N, T, E)                                                                                 \
     hipLaunchKernelGGL((k_step_chain<kChainU, P, D, N, T, E>), grid, dim3(kThreads), 0, stream, state, x0c, x0u, \
-                       eps_c, eps_u, a, ch, pre_disc)
+                       eps_c, eps_u, a, ch, pre_disc, first)
 #define PC_CHAIN_E(P, D, N, T) \
     if (eps) PC_CHAIN(P, D, N, T, true); else PC_CHAIN(P, D, N, T, false)
 #define PC_CHAIN_NT(P, D, N) \
     if (nt) PC_CHAIN_E(P, D, N, true); else PC_CHAIN_E(P, D, N, false)
-    if (init) {  // the whole-loop entry point's first step: projecting, no discrepancy, references
+        if (init) {  // the whole-loop entry point's first step: projecting, no discrepancy, references
 #define PC_CHAIN_INIT(N, T)                                                                                    \
     hipLaunchKernelGGL((k_step_chain<kChainU, true, false, N, T, false, true>), grid, dim3(kThreads), 0, stream, \
-                       state, x0c, x0u, eps_c, eps_u, a, ch, pre_disc)
-        if (noise) {
-            if (nt) PC_CHAIN_INIT(true, true); else PC_CHAIN_INIT(true, false);
-        } else {
-            if (nt) PC_CHAIN_INIT(false, true); else PC_CHAIN_INIT(false, false);
-        }
+                       state, x0c, x0u, eps_c, eps_u, a, ch, pre_disc, first)
+            if (noise) {
+                if (nt) PC_CHAIN_INIT(true, true); else PC_CHAIN_INIT(true, false);
+            } else {
+                if (nt) PC_CHAIN_INIT(false, true); else PC_CHAIN_INIT(false, false);
+            }
 #undef PC_CHAIN_INIT
-    } else if (project) {
-        if (disc) {
-            if (noise) PC_CHAIN_NT(true, true, true); else PC_CHAIN_NT(true, true, false);
+        } else if (project) {
+            if (disc) {
+                if (noise) PC_CHAIN_NT(true, true, true); else PC_CHAIN_NT(true, true, false);
+            } else {
+                if (noise) PC_CHAIN_NT(true, false, true); else PC_CHAIN_NT(true, false, false);
+            }
         } else {
-            if (noise) PC_CHAIN_NT(true, false, true); else PC_CHAIN_NT(true, false, false);
+            if (noise) PC_CHAIN_NT(false, true, true); else PC_CHAIN_NT(false, true, false);
         }
-    } else {
-        if (noise) PC_CHAIN_NT(false, true, true); else PC_CHAIN_NT(false, true, false);
-    }
 #undef PC_CHAIN_NT
 #undef PC_CHAIN_E
 #undef PC_CHAIN
-    return hipGetLastError();
+    });
 }
 
 }  // namespace pc

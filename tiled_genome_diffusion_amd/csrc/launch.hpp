@@ -3,8 +3,24 @@
 #pragma once
 
 #include "common.hpp"
+#include "dispatch.hpp"
 
 namespace pc {
+
+// Work-items per dispatch in force: the hardware's 2^32 - 1, or the lower cap
+// set by the diagnostic pc_set_max_dispatch_items (api.hip).
+uint64_t dispatch_items();
+
+// Launches a grid of n_blocks workgroups of `threads` lanes as consecutive
+// slices within the dispatch cap; launch(first, count) enqueues one slice
+// whose kernel adds `first` to its workgroup index.
+template <class F>
+hipError_t launch_slices(int64_t n_blocks, int threads, F &&launch) {
+    return for_each_slice(n_blocks, threads, dispatch_items(), hipSuccess, [&](int64_t first, uint32_t count) {
+        launch(first, count);
+        return hipGetLastError();
+    });
+}
 
 hipError_t launch_fill(void *out, int64_t n_maps, uint32_t k0, uint32_t k1, uint32_t slot, bool raw,
                        hipStream_t stream);

@@ -386,12 +386,12 @@ __device__ __forceinline__ void stage_map(const float *maps, size_t m, float4 *s
 
 // One map per 64-lane workgroup, lane i owning bead i.
 __global__ __launch_bounds__(kLanes, 4) void k_mds(const float *__restrict__ maps, float *__restrict__ coords,
-                                                float *__restrict__ eigvals, int32_t max_iters) {
+                                                float *__restrict__ eigvals, int32_t max_iters, int64_t block0) {
     __shared__ float4 s_map[kQuads];
     __shared__ float4 s_q[kBeads];
     __shared__ __align__(16) float s_mean[kBeads];
     const int i = threadIdx.x;
-    const size_t m = blockIdx.x;
+    const size_t m = static_cast<size_t>(block0) + blockIdx.x;
     stage_map(maps, m, s_map, i);
     __syncthreads();
     const float *xs = reinterpret_cast<const float *>(s_map);
@@ -469,10 +469,9 @@ __global__ __launch_bounds__(kLanes, 4) void k_mds(const float *__restrict__ map
 
 hipError_t launch_mds(const float *maps, int64_t n_maps, float *coords, float *eigvals, int32_t max_iters,
                       hipStream_t stream) {
-    if (n_maps == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_mds, dim3(static_cast<uint32_t>(n_maps)), dim3(kLanes), 0, stream, maps, coords, eigvals,
-                       max_iters);
-    return hipGetLastError();
+    return launch_slices(n_maps, kLanes, [&](int64_t first, uint32_t count) {
+        hipLaunchKernelGGL(k_mds, dim3(count), dim3(kLanes), 0, stream, maps, coords, eigvals, max_iters, first);
+    });
 }
 
 }  // namespace pc

@@ -17,8 +17,8 @@ __device__ __forceinline__ void pair_indices(int p, int O, int &lidx, int &ridx)
 
 // One lane per (chain, seam, column, pair).
 __global__ __launch_bounds__(256) void k_seam_project(float *__restrict__ state, int64_t total, int32_t n_cols,
-                                                      ChainArgs ch) {
-    const int64_t it = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+                                                      ChainArgs ch, int64_t block0) {
+    const int64_t it = (block0 + blockIdx.x) * blockDim.x + threadIdx.x;
     if (it >= total) return;
     const int NP = ch.n_pairs, L = ch.chain_len;
     const int p = static_cast<int>(it % NP);
@@ -44,8 +44,9 @@ constexpr int kDiscThreads = 256;
 constexpr int kDiscWaves = kDiscThreads / 64;
 
 __global__ __launch_bounds__(kDiscThreads) void k_seam_disc(const float *__restrict__ state, int64_t total,
-                                                            int32_t n_cols, ChainArgs ch, float *__restrict__ rms) {
-    const int64_t sc = static_cast<int64_t>(blockIdx.x) * kDiscWaves + (threadIdx.x >> 6);
+                                                            int32_t n_cols, ChainArgs ch, float *__restrict__ rms,
+                                                            int64_t block0) {
+    const int64_t sc = (block0 + blockIdx.x) * kDiscWaves + (threadIdx.x >> 6);
     if (sc >= total) return;  // uniform over the wavefront
     const int lane = static_cast<int>(threadIdx.x) & 63;
     const int L = ch.chain_len, NP = ch.n_pairs;
@@ -74,12 +75,14 @@ __global__ __launch_bounds__(kDiscThreads) void k_seam_disc(const float *__restr
 constexpr int kMeanAbsThreads = 1024;
 
 __global__ __launch_bounds__(kMeanAbsThreads) void k_seam_mean_abs(const float *__restrict__ state, int32_t G,
-                                                                  int32_t S, ChainArgs ch, float *__restrict__ out) {
+                                                                  int32_t S, ChainArgs ch, float *__restrict__ out,
+                                                                  int64_t block0) {
     __shared__ double s_l[kMeanAbsThreads], s_r[kMeanAbsThreads];
     const int NP = ch.n_pairs, L = ch.chain_len;
     const int J = kMeanAbsThreads / NP;
-    const int cj = static_cast<int>(blockIdx.x) / G;   // c (L - 1) + seam
-    const int g = static_cast<int>(blockIdx.x) - cj * G;
+    const int64_t blk = block0 + blockIdx.x;            // (c (L - 1) + seam) G + g
+    const int cj = static_cast<int>(blk / G);           // c (L - 1) + seam
+    const int g = static_cast<int>(blk - static_cast<int64_t>(cj) * G);
     const int c = cj / (L - 1);
     const int seam = cj - c * (L - 1);
     const int n_cols = G * S;
@@ -126,7 +129,7 @@ __global__ __launch_bounds__(kMeanAbsThreads) void k_seam_mean_abs(const float *
         if (t < h) s_l[t] += s_l[t + h];
         __syncthreads();
     }
-    if (t == 0) out[blockIdx.x] = static_cast<float>(s_l[0] / NP);
+    if (t == 0) out[blk] = static_cast<float>(s_l[0] / NP);
 }
 
 // Mean and max of n values by one workgroup: each lane folds a strided slice
@@ -176,37 +179,31 @@ __global__ __launch_bounds__(kMeanMaxThreads) void k_mean_max(const float *__res
 
 hipError_t launch_seam_project(float *state, int32_t n_chains, int32_t n_cols, ChainArgs ch, hipStream_t stream) {
     const int64_t total = static_cast<int64_t>(n_chains) * (ch.chain_len - 1) * n_cols * ch.n_pairs;
-    if (total == 0) return hipSuccess;
-    const int64_t blocks = (total + 255) / 256;
-    hipLaunchKernelGGL(k_seam_project, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream, state, total,
-                       n_cols, ch);
-    return hipGetLastError();
+    return launch_slices((total + 255) / 256, 256, [&](int64_t first, uint32_t count) {
+        hipLaunchKernelGGL(k_seam_project, dim3(count), dim3(256), 0, stream, state, total, n_cols, ch, first);
+    });
 }
 
 hipError_t launch_seam_mean_abs(const float *state, int32_t n_chains, int32_t G, int32_t S, ChainArgs ch, float *out,
                                 hipStream_t stream) {
     const int64_t blocks = static_cast<int64_t>(n_chains) * (ch.chain_len - 1) * G;
-    if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_seam_mean_abs, dim3(static_cast<uint32_t>(blocks)), dim3(kMeanAbsThreads), 0, stream, state,
-                       G, S, ch, out);
-    return hipGetLastError();
+    return launch_slices(blocks, kMeanAbsThreads, [&](int64_t first, uint32_t count) {
+        hipLaunchKernelGGL(k_seam_mean_abs, dim3(count), dim3(kMeanAbsThreads), 0, stream, state, G, S, ch, out,
+                           first);
+    });
 }
 
 hipError_t launch_seam_discrepancy(const float *state, int32_t n_chains, int32_t n_cols, ChainArgs ch, float *rms,
                                    float *summary, hipStream_t stream) {
     const int64_t total = static_cast<int64_t>(n_chains) * (ch.chain_len - 1) * n_cols;
-    if (total > 0) {
-        const int64_t blocks = (total + kDiscWaves - 1) / kDiscWaves;
-        hipLaunchKernelGGL(k_seam_disc, dim3(static_cast<uint32_t>(blocks)), dim3(kDiscThreads), 0, stream, state,
-                           total, n_cols, ch, rms);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    if (summary) {
-        hipLaunchKernelGGL(k_mean_max, dim3(1), dim3(kMeanMaxThreads), 0, stream, rms, total, summary);
-        return hipGetLastError();
-    }
-    return hipSuccess;
+    const hipError_t e = launch_slices((total + kDiscWaves - 1) / kDiscWaves, kDiscThreads,
+                                       [&](int64_t first, uint32_t count) {
+        hipLaunchKernelGGL(k_seam_disc, dim3(count), dim3(kDiscThreads), 0, stream, state, total, n_cols, ch, rms,
+                           first);
+    });
+    if (e != hipSuccess || !summary) return e;
+    hipLaunchKernelGGL(k_mean_max, dim3(1), dim3(kMeanMaxThreads), 0, stream, rms, total, summary);
+    return hipGetLastError();
 }
 
 }  // namespace pc

@@ -167,12 +167,13 @@ __device__ float fit(const float *x, const float *y, int O, float (&t)[12]) {
 
 __global__ __launch_bounds__(kStitchThreads) void k_stitch(const float *__restrict__ coords, int32_t G, int32_t S,
                                                            ChainArgs ch, float *__restrict__ chain,
-                                                           float *__restrict__ resid) {
+                                                           float *__restrict__ resid, int64_t block0) {
     extern __shared__ float s_t[];  // [L][12]: chunk-local scans, then T_k; [16][12]: chunk totals, then carries
     const int wave = static_cast<int>(threadIdx.x) >> 6, lane = static_cast<int>(threadIdx.x) & 63;
     const int n_cols = G * S;
-    const int c = static_cast<int>(blockIdx.x) / n_cols;
-    const int gs = static_cast<int>(blockIdx.x) - c * n_cols;
+    const int64_t blk = block0 + blockIdx.x;  // joint sample c n_cols + gs
+    const int c = static_cast<int>(blk / n_cols);
+    const int gs = static_cast<int>(blk - static_cast<int64_t>(c) * n_cols);
     const int L = ch.chain_len, O = ch.overlap, stride = kBeads - O;
     const int n_beads = (L - 1) * stride + kBeads;
     const int n_chunks = (L + 63) >> 6;
@@ -268,13 +269,13 @@ __global__ __launch_bounds__(kStitchThreads) void k_stitch(const float *__restri
 
 hipError_t launch_stitch(const float *coords, int32_t n_chains, int32_t G, int32_t S, ChainArgs ch, float *chain,
                          float *resid, hipStream_t stream) {
-    const int64_t blocks = static_cast<int64_t>(n_chains) * G * S;
-    if (blocks == 0) return hipSuccess;
     if (ch.chain_len > 64 * kStitchMaxChunks) return hipErrorInvalidValue;
+    const int64_t blocks = static_cast<int64_t>(n_chains) * G * S;
     const size_t lds = static_cast<size_t>(ch.chain_len + kStitchMaxChunks) * 12 * sizeof(float);
-    hipLaunchKernelGGL(k_stitch, dim3(static_cast<uint32_t>(blocks)), dim3(kStitchThreads), lds, stream, coords, G, S,
-                       ch, chain, resid);
-    return hipGetLastError();
+    return launch_slices(blocks, kStitchThreads, [&](int64_t first, uint32_t count) {
+        hipLaunchKernelGGL(k_stitch, dim3(count), dim3(kStitchThreads), lds, stream, coords, G, S, ch, chain, resid,
+                           first);
+    });
 }
 
 }  // namespace pc
