@@ -32,7 +32,7 @@ int block0_arg(const std::string &name) {
         int arg;
     } table[] = {{"k_fill", 6},          {"k_step_indep", 6}, {"k_step_chain", 8},
                  {"k_seam_project", 4},  {"k_seam_disc", 5},  {"k_seam_mean_abs", 5},
-                 {"k_mds", 4},           {"k_stitch", 6}};
+                 {"k_mds", 6},           {"k_stitch", 6}};
     for (const auto &t : table)
         if (name.find(t.kernel) != std::string::npos) return t.arg;
     return -1;
