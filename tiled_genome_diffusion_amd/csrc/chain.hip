@@ -11,6 +11,9 @@ constexpr int kChainU = 1;           // maps per lane per barrier, chain layout 
 // clocks: 6 is best for both the 16,384-map and the 32,000-map chain (41.8 and
 // 76.2 us per step; 8 maps: 41.8 and 78.8; 4: 44 and 80; 10: 44.8 and 80.6).
 constexpr int kChainMaps = 6;
+// The wavefront that sums the pre-projection discrepancy: the last one, which
+// holds the right-seam lines and the idle lanes past the map's 504 quads.
+constexpr uint32_t kDiscWave = kThreads / 64 - 1;
 
 // Workgroups are laid out as for independent maps: one workgroup
 // steps a.maps_per_block maps of one tile k (region r = c L + k) and weight g.
@@ -31,8 +34,9 @@ constexpr int kChainMaps = 6;
 //     whole float4 quads.
 // Every quad is stepped once, every store is a full float4, no cache line is
 // written by two workgroups, and every lane runs exactly one stepping task
-// per map.  With DISC an otherwise idle lane per map sums the squared seam
-// differences in pair order and stores the RMS per (seam, g, s).  LDS is
+// per map.  With DISC the last wavefront sums the squared seam differences,
+// pairs strided over its lanes and a fixed DPP tree across them, and stores
+// the RMS per (seam, g, s) of its maps after the loop.  LDS is
 // double-buffered by iteration parity, so one barrier per iteration
 // suffices.  INIT (the projecting first step of a run) draws x_T in
 // registers instead of reading a filled state.
@@ -42,7 +46,6 @@ __global__ __launch_bounds__(kThreads) void k_step_chain(float *__restrict__ sta
                                                          const float *__restrict__ eps_c,
                                                          const float *__restrict__ eps_u, StepArgs a, ChainArgs ch,
                                                          float *__restrict__ pre_disc, int64_t block0) {
-    static_assert(U <= kThreads - kQuads, "the discrepancy of map u is summed by idle lane kQuads + u");
     __shared__ float s_right[2][U][kMaxPairs];  // tile k's stepped right-seam values
     __shared__ float s_left[2][U][kMaxPairs];   // tile k+1's stepped left-seam values
 
@@ -110,6 +113,9 @@ __global__ __launch_bounds__(kThreads) void k_step_chain(float *__restrict__ sta
     const int s0 = chunk * a.maps_per_block;
     const int s1 = s0 + a.maps_per_block < a.S ? s0 + a.maps_per_block : a.S;
     const size_t t_base = static_cast<size_t>(rg) * a.S;
+    // DISC: lane j of the last wavefront keeps map s0 + j's discrepancy, stored after the loop (a
+    // store inside the loop makes every map wait for the previous map's stores to complete)
+    float disc_keep = 0.f;
     int par = 0;
     for (int sb = s0; sb < s1; sb += U, par ^= 1) {
         const int nu = s1 - sb < U ? s1 - sb : U;
@@ -174,17 +180,21 @@ __global__ __launch_bounds__(kThreads) void k_step_chain(float *__restrict__ sta
                 }
             }
             if (active) st_state<NT>(state, (map + off0) * kQuads + q, y0[u]);
-            if (DISC && owns_seam && static_cast<int>(q) == kQuads + u) {  // an otherwise idle lane
+            if (DISC && owns_seam && (q >> 6) == kDiscWave) {  // wave-uniform: the last wavefront
+                const int lane = static_cast<int>(q & 63);
                 float acc = 0.f;
-                for (int p = 0; p < NP; ++p) {
+                for (int p = lane; p < NP; p += 64) {
                     const float d = s_right[par][u][p] - s_left[par][u][p];
                     acc = fmaf(d, d, acc);
                 }
-                pre_disc[(static_cast<size_t>(c) * (L - 1) + k) * n_cols + static_cast<size_t>(g) * a.S + sb + u] =
-                    sqrtf(acc / static_cast<float>(NP));
+                const float sum = wave_sum(acc);
+                disc_keep = lane == sb + u - s0 ? sqrtf(sum / static_cast<float>(NP)) : disc_keep;
             }
         }
     }
+    if (DISC && owns_seam && (q >> 6) == kDiscWave && static_cast<int>(q & 63) < s1 - s0)
+        pre_disc[(static_cast<size_t>(c) * (L - 1) + k) * n_cols + static_cast<size_t>(g) * a.S + s0 + (q & 63)] =
+            disc_keep;
 }
 
 }  // namespace

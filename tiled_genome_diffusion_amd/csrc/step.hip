@@ -34,37 +34,8 @@ __global__ __launch_bounds__(kThreads) void k_fill(void *__restrict__ out, int64
 }
 
 // ---------------------------------------------------------------------------
-// Independent maps: workgroup -> (region r, weight g, chunk of trajectories).
-// U maps are loaded before any is computed, to keep U loads in flight.  EPS:
-// the noise predictions of each map are read from eps_c / eps_u (same layout
-// as the state) instead of being formed from the region's references.
-template <int U, bool NOISE, bool NT, bool EPS>
-__device__ __forceinline__ void step_maps(float *__restrict__ state, const float *__restrict__ eps_c,
-                                          const float *__restrict__ eps_u, size_t map0, uint32_t t0, uint32_t q,
-                                          float4 xc, float4 xu, float w, const StepArgs &a) {
-    float4 x[U], ec[U], eu[U];
-    if (a.init) {  // first step of a run: x_T is drawn here, not read (wave-uniform)
-#pragma unroll
-        for (int u = 0; u < U; ++u) x[u] = philox_normals(q, t0 + u, 0u, a.k0, a.k1);
-    } else {
-#pragma unroll
-        for (int u = 0; u < U; ++u) x[u] = ld_state<NT>(state, (map0 + u) * kQuads + q);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        if (EPS) {
-            ec[u] = ld_state<NT>(eps_c, (map0 + u) * kQuads + q);
-            eu[u] = ld_state<NT>(eps_u, (map0 + u) * kQuads + q);
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const float4 z = NOISE ? philox_normals(q, t0 + u, a.slot, a.k0, a.k1) : make_float4(0.f, 0.f, 0.f, 0.f);
-        st_state<NT>(state, (map0 + u) * kQuads + q,
-                     EPS ? step4<true>(x[u], ec[u], eu[u], w, a.c, z) : step4<false>(x[u], xc, xu, w, a.c, z));
-    }
-}
-
+// Independent maps: workgroup -> (region r, weight g, chunk of trajectories),
+// each lane stepping its quad of the chunk's maps (step_maps, stream.hpp).
 template <int U, bool NOISE, bool NT, bool EPS>
 __global__ __launch_bounds__(kThreads) void k_step_indep(float *__restrict__ state, const float *__restrict__ x0c,
                                                          const float *__restrict__ x0u,

@@ -70,4 +70,36 @@ __device__ __forceinline__ float4 step4(float4 x, float4 dc, float4 du, float w,
     return y;
 }
 
+// Steps quad q of maps map0 .. map0 + U - 1 (trajectory ids t0 ..), U loads
+// in flight before any is computed.  EPS: the noise predictions of each map
+// are read from eps_c / eps_u (same layout as the state) instead of being
+// formed from the region's references xc / xu.  With a.init (the first step
+// of a run, wave-uniform) x_T is drawn from Philox slot 0 instead of read.
+template <int U, bool NOISE, bool NT, bool EPS>
+__device__ __forceinline__ void step_maps(float *__restrict__ state, const float *__restrict__ eps_c,
+                                          const float *__restrict__ eps_u, size_t map0, uint32_t t0, uint32_t q,
+                                          float4 xc, float4 xu, float w, const StepArgs &a) {
+    float4 x[U], ec[U], eu[U];
+    if (a.init) {  // first step of a run: x_T is drawn here, not read (wave-uniform)
+#pragma unroll
+        for (int u = 0; u < U; ++u) x[u] = philox_normals(q, t0 + u, 0u, a.k0, a.k1);
+    } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) x[u] = ld_state<NT>(state, (map0 + u) * kQuads + q);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (EPS) {
+            ec[u] = ld_state<NT>(eps_c, (map0 + u) * kQuads + q);
+            eu[u] = ld_state<NT>(eps_u, (map0 + u) * kQuads + q);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const float4 z = NOISE ? philox_normals(q, t0 + u, a.slot, a.k0, a.k1) : make_float4(0.f, 0.f, 0.f, 0.f);
+        st_state<NT>(state, (map0 + u) * kQuads + q,
+                     EPS ? step4<true>(x[u], ec[u], eu[u], w, a.c, z) : step4<false>(x[u], xc, xu, w, a.c, z));
+    }
+}
+
 }  // namespace pc
