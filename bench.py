@@ -768,7 +768,7 @@ def main():
                      "bytes_per_steady_launch": bytes_per_launch,
                      # measured live: the step's state access pattern with one FMA per element
                      "ceiling": probes["rmw_gbs"], "frac_of_ceiling": achieved / probes["rmw_gbs"],
-                     "ceiling_kind": "in-place non-temporal float4 read-modify-write probe, step kernel's mapping",
+                     "ceiling_kind": "in-place float4 read-modify-write probe, step kernel's mapping and cache policy",
                      "read_ceiling": probes["read_gbs"], "write_ceiling": probes["write_gbs"]},
         "value_by_seed": by_seed,
         "value_sd_over_seeds": float(np.std(list(by_seed.values()), ddof=1)) if len(by_seed) > 1 else None,
