@@ -206,7 +206,10 @@ def probe_lib():
 
 def hbm_probes(state, n_maps, stream, reps=5):
     """GB/s of the three probes over `state` (n_maps packed maps; overwritten), each the median
-    of `reps` launches timed with HIP events on `stream`, after one untimed launch."""
+    of `reps` timings with HIP events on `stream`, after one untimed launch.  A timing spans one
+    launch for states of 1 GB and more, and 20 back-to-back launches for smaller ones, whose
+    launches last tens of microseconds: one launch between two events would also time the
+    launch latency, which back-to-back launches of the step loop do not pay."""
     import ctypes
 
     import numpy as np
@@ -224,14 +227,16 @@ def hbm_probes(state, n_maps, stream, reps=5):
     for name, (fn, moved) in calls.items():
         if fn() != 0:
             raise RuntimeError(f"probe {name} failed to launch")
+        per = 1 if nbytes >= 1 << 30 else 20
         times = []
         for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            fn()
+            for _ in range(per):
+                fn()
             e1.record(stream)
             torch.cuda.synchronize()
-            times.append(e0.elapsed_time(e1) * 1e-3)
+            times.append(e0.elapsed_time(e1) * 1e-3 / per)
         out[name + "_gbs"] = moved / float(np.median(times)) / 1e9
     return out
 
