@@ -28,3 +28,7 @@ def pytest_terminal_summary(terminalreporter):
         terminalreporter.write_line(
             f"largest relative MDS distance error over {gu.WORST['dist_checks']} maps: "
             f"{gu.WORST['dist']:.3e} (bound 1e-4)")
+    if gu is not None and gu.WORST_BY_TEST:
+        terminalreporter.write_line("largest error per test (kind, test, error):")
+        for (kind, test), err in sorted(gu.WORST_BY_TEST.items()):
+            terminalreporter.write_line(f"  {kind:5s} {test} {err:.3e}")

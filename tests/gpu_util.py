@@ -3,6 +3,7 @@ seeded inputs and comparing with the oracle."""
 
 from __future__ import annotations
 
+import os
 import sys
 
 import numpy as np
@@ -41,8 +42,16 @@ def map_index(wl: Workload, r: int, g: int, s: int) -> int:
     return (r * wl.n_guidance + g) * wl.n_traj + s
 
 
-# Largest normwise state error seen by any parity check of the session (reported at the end).
+# Largest normwise state error seen by any parity check of the session (reported at the end),
+# and the largest of each kind per test.
 WORST = {"state": 0.0, "checks": 0, "dist": 0.0, "dist_checks": 0}
+WORST_BY_TEST: dict = {}
+
+
+def _note(kind: str, err: float) -> None:
+    test = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
+    key = (kind, test)
+    WORST_BY_TEST[key] = max(WORST_BY_TEST.get(key, 0.0), err)
 
 
 def normwise_err(gpu: np.ndarray, ref: np.ndarray) -> float:
@@ -53,6 +62,7 @@ def normwise_err(gpu: np.ndarray, ref: np.ndarray) -> float:
     err = float((np.abs(g - r).max(axis=1) / scale).max())
     WORST["state"] = max(WORST["state"], err)
     WORST["checks"] += 1
+    _note("state", err)
     return err
 
 
@@ -61,6 +71,7 @@ def rel_dist_err(dist_gpu: np.ndarray, dist_ref: np.ndarray) -> float:
     err = float(np.abs(np.asarray(dist_gpu) - np.asarray(dist_ref)).max() / np.asarray(dist_ref).max())
     WORST["dist"] = max(WORST["dist"], err)
     WORST["dist_checks"] += 1
+    _note("dist", err)
     return err
 
 
