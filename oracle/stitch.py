@@ -14,6 +14,12 @@ diagnostic).  Readings used here:
   alignment;
 * a bead shared by two tiles takes the mean of its two aligned positions.
 
+The alternative reading, Kabsch's fit restricted to proper rotations
+(det = +1, the determinant correction of the SVD solution), is available with
+``proper=True``: where the best orthogonal map is a reflection, the sign of
+the singular direction of the smallest singular value is flipped, which costs
+4 sigma_3 in the sum of squared distances (the trace form of the objective).
+
 Tile 0 keeps its own frame.  Shapes: tiles [L, 64, 3] -> chain
 [(L-1)(64-O) + 64, 3] and residuals [L-1].
 """
@@ -23,17 +29,20 @@ from __future__ import annotations
 import numpy as np
 
 
-def align(x, y):
-    """(R, shift): y ~ x @ R + shift, R orthogonal (3x3), minimising the squared error."""
+def align(x, y, proper: bool = False):
+    """(R, shift): y ~ x @ R + shift, R orthogonal (3x3; a rotation with proper=True),
+    minimising the squared error."""
     x = np.asarray(x, dtype=np.float64)
     y = np.asarray(y, dtype=np.float64)
     xm, ym = x.mean(axis=0), y.mean(axis=0)
     u, _, vt = np.linalg.svd((x - xm).T @ (y - ym))
     r = u @ vt
+    if proper and np.linalg.det(r) < 0:
+        r = u @ np.diag([1.0, 1.0, -1.0]) @ vt
     return r, ym - xm @ r
 
 
-def stitch_chain(tiles, overlap: int):
+def stitch_chain(tiles, overlap: int, proper: bool = False):
     tiles = np.asarray(tiles, dtype=np.float64)
     L, n, _ = tiles.shape
     stride = n - overlap
@@ -45,7 +54,7 @@ def stitch_chain(tiles, overlap: int):
     count[:n] += 1
     for k in range(1, L):
         x = tiles[k]
-        r, shift = align(x[:overlap], prev[n - overlap:])
+        r, shift = align(x[:overlap], prev[n - overlap:], proper)
         cur = x @ r + shift
         d = cur[:overlap] - prev[n - overlap:]
         resid[k - 1] = np.sqrt(np.mean(np.sum(d * d, axis=1)))
