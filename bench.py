@@ -441,11 +441,13 @@ def chain_kernels(args, wl, n_steps):
     n_beads = (wl.chain_len - 1) * (64 - wl.overlap) + 64
     chain = torch.empty(n_chains * n_cols * n_beads * 3, dtype=torch.float32, device=dev)
     resid = torch.empty(lay.n_seams * n_cols, dtype=torch.float32, device=dev)
+    resid_p = torch.empty_like(resid)
     rms = torch.empty(lay.n_seams * n_cols, dtype=torch.float32, device=dev)
     summary = torch.empty(2, dtype=torch.float32, device=dev)
     mean_abs = torch.empty(lay.n_seams * wl.n_guidance, dtype=torch.float32, device=dev)
     calls = {
         "pc_kabsch_stitch": lambda: pc.pc_kabsch_stitch(coords, lay, chain, resid),
+        "pc_kabsch_stitch_proper": lambda: pc.pc_kabsch_stitch_proper(coords, lay, chain, resid_p),
         "pc_seam_mean_abs": lambda: pc.pc_seam_mean_abs(state, lay, mean_abs),
         "pc_seam_discrepancy": lambda: pc.pc_seam_discrepancy(state, lay, rms, summary),
         "pc_seam_project": lambda: pc.pc_seam_project(state, lay),
@@ -467,7 +469,10 @@ def chain_kernels(args, wl, n_steps):
     print(json.dumps({"metric": "chain kernels, microseconds per call", "workload": wl.name,
                       "chains": n_chains, "joint_samples_per_chain": n_cols, "chain_beads": n_beads,
                       "us_per_call": rows,
-                      "max_seam_residual": float(resid.max()), "post_projection_rms_max": float(summary[1])}),
+                      "max_seam_residual": float(resid.max()),
+                      "rotations_only": {"max_seam_residual": float(resid_p.max()),
+                                         "mirrored_seams": int((resid_p > 1e-2).sum())},
+                      "post_projection_rms_max": float(summary[1])}),
           flush=True)
 
 

@@ -270,6 +270,18 @@ PC_API pc_status pc_mds_recover(const float *maps, int64_t n_maps, float *coords
 PC_API pc_status pc_kabsch_stitch(const float *coords, const pc_layout *layout, float *chain, float *residual,
                                   void *stream);
 
+/*
+ * The same stitching with every fit restricted to rotations (det +1): Kabsch's
+ * fit with the determinant correction, the other reading of the Kabsch
+ * alignment of section 5.5 and Figure 4.  Where the best orthogonal map of a
+ * seam is a reflection (adjacent tiles recovered as mirror images), the best
+ * rotation is taken instead and the seam keeps a residual of the order of the
+ * shared block's size: mirrored tiles are not superposed.  Arguments, layout
+ * and errors as pc_kabsch_stitch.
+ */
+PC_API pc_status pc_kabsch_stitch_proper(const float *coords, const pc_layout *layout, float *chain, float *residual,
+                                         void *stream);
+
 /* Diagnostics ----------------------------------------------------------- */
 
 /*

@@ -215,6 +215,11 @@ void validation() {
     const pc_layout coplanar = lay(4, 1, 1, 4, 3);
     CHECK(pc_kabsch_stitch(F, &coplanar, F2, F2, nullptr) == PC_ERR_SHAPE);
     CHECK(pc_kabsch_stitch(F, &ch, nullptr, F2, nullptr) == PC_ERR_NULL);
+    CHECK(pc_kabsch_stitch_proper(F, &ok, F2, F2, nullptr) == PC_ERR_SHAPE);
+    CHECK(pc_kabsch_stitch_proper(F, &long_chain, F2, F2, nullptr) == PC_ERR_SHAPE);
+    CHECK(pc_kabsch_stitch_proper(F, &coplanar, F2, F2, nullptr) == PC_ERR_SHAPE);
+    CHECK(pc_kabsch_stitch_proper(F, &ch, F2, nullptr, nullptr) == PC_ERR_NULL);
+    CHECK(pc_kabsch_stitch_proper(F, &ch, F2, MIS, nullptr) == PC_ERR_ALIGN);
     CHECK(pc_set_max_dispatch_items(1023) == PC_ERR_PARAM);
     CHECK(pc_set_max_dispatch_items(kCap + 1) == PC_ERR_PARAM);
     CHECK(pc_seam_index_map(nullptr, 12) == PC_ERR_NULL);
@@ -288,6 +293,11 @@ void geometry(const pc_layout &L, uint64_t cap) {
         stub::reset();
         CHECK(pc_kabsch_stitch(F, &L, F2, F, nullptr) == PC_OK);
         EXPECT_GRIDS("k_stitch", n_chains * G * S, 256, 1, cap);
+        for (const auto &l : stub::launches) CHECK(l.kernel.find("k_stitchILb0E") != std::string::npos);
+        stub::reset();
+        CHECK(pc_kabsch_stitch_proper(F, &L, F2, F, nullptr) == PC_OK);
+        EXPECT_GRIDS("k_stitch", n_chains * G * S, 256, 1, cap);
+        for (const auto &l : stub::launches) CHECK(l.kernel.find("k_stitchILb1E") != std::string::npos);
     }
 }
 

@@ -110,6 +110,9 @@ def test_chain_entry_points_split_bitwise(capped, cap):
         resid = torch.empty(n_seam_cols, dtype=torch.float32, device=dev)
         pc.pc_kabsch_stitch(coords, lay, chain, resid)
         out["chain"], out["resid"] = chain, resid
+        chain_p, resid_p = torch.empty_like(chain), torch.empty_like(resid)
+        pc.pc_kabsch_stitch_proper(coords, lay, chain_p, resid_p)
+        out["chain_proper"], out["resid_proper"] = chain_p, resid_p
         torch.cuda.synchronize()
         return out
 

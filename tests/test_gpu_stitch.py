@@ -53,6 +53,64 @@ def test_stitch_synthetic_rigid_motions(L, O, n_chains, S):
             assert np.all(res[c, :, s] <= 1e-4 * ext) and np.all(wres <= 1e-5 * ext)
 
 
+def _rot(rng):
+    q = _orth(rng, False)
+    if np.linalg.det(q) < 0:
+        q[:, 0] *= -1
+    return q
+
+
+@pytest.mark.parametrize("mirror_every", [0, 3], ids=["rotations", "mirrored-tiles"])
+def test_stitch_proper_matches_oracle(mirror_every):
+    """Stitching restricted to rotations (det +1) against the oracle's Kabsch fit with the
+    determinant correction.  Tiles moved by rotations only are stitched exactly; a mirrored
+    tile cannot be superposed, and its seams keep a residual of the order of the shared
+    block's size.  Residuals are compared everywhere; a mirrored seam's rotation is unique
+    only when the two smallest singular values of its cross-covariance are apart, so chain
+    coordinates are compared up to the first seam where they are not."""
+    torch, dev = torch_dev()
+    rng = np.random.default_rng(5 + mirror_every)
+    L, O, S = 9, 12, 6
+    stride = 64 - O
+    lay = pc.PCLayout(L, 1, S, L, O)
+    say(f"stitch, rotations only: L={L} O={O} S={S}, every {mirror_every or 'no'}th tile mirrored")
+    coords = np.zeros((L, 1, S, 64, 3), dtype=np.float32)
+    for s in range(S):
+        walk = random_walk((L - 1) * stride + 64, walk_rng(s, 3, 91), None)
+        for k in range(L):
+            m = _rot(rng)
+            if mirror_every and k % mirror_every == mirror_every - 1:
+                m = m @ np.diag([1.0, 1.0, -1.0])
+            coords[k, 0, s] = walk[k * stride:k * stride + 64] @ m + rng.standard_normal(3) * 5
+    cd = torch.from_numpy(coords.reshape(-1)).to(dev)
+    nb = (L - 1) * stride + 64
+    chain = torch.empty(S * nb * 3, dtype=torch.float32, device=dev)
+    resid = torch.empty((L - 1) * S, dtype=torch.float32, device=dev)
+    pc.pc_kabsch_stitch_proper(cd, lay, chain, resid)
+    got = chain.cpu().numpy().reshape(S, nb, 3)
+    res = resid.cpu().numpy().reshape(L - 1, S)
+    for s in range(S):
+        tiles = coords[:, 0, s].astype(np.float64)
+        want, wres = stitch.stitch_chain(tiles, O, proper=True)
+        ext = np.abs(want).max()
+        assert np.allclose(res[:, s], wres, atol=1e-4 * ext, rtol=1e-3)
+        if not mirror_every:
+            assert np.all(wres <= 1e-5 * ext) and np.abs(got[s] - want).max() <= 1e-4 * ext
+            continue
+        assert wres.max() > 0.05
+        # compare the chain up to the first tile whose fit is not unique to float32 precision
+        upto = L
+        for k in range(1, L):
+            x, y = tiles[k][:O], tiles[k - 1][stride:]
+            sig = np.linalg.svd((x - x.mean(0)).T @ (y - y.mean(0)), compute_uv=False)
+            if (sig[1] - sig[2]) < 0.05 * sig[0]:
+                upto = k
+                break
+        n_ok = (upto - 1) * stride + 64 - (O if upto < L else 0)
+        assert upto >= 2
+        assert np.abs(got[s, :n_ok] - want[:n_ok]).max() <= 1e-4 * ext
+
+
 def test_stitch_end_to_end_chr22():
     torch, dev = torch_dev()
     wl = get("chr22_chain")

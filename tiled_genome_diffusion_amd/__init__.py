@@ -17,7 +17,7 @@ from . import _lib
 
 __all__ = ["PCError", "PCLayout", "PACKED", "BEADS", "pc_version", "pc_last_error", "pc_ddim_schedule",
            "pc_ddim_schedule_cosine", "pc_init_state", "pc_ddim_cfg_step", "pc_ddim_cfg_step_eps", "pc_ddim_sample", "pc_seam_project", "pc_seam_discrepancy",
-           "pc_seam_mean_abs", "pc_mds_recover", "pc_kabsch_stitch", "pc_set_max_dispatch_items", "pc_philox_block", "pc_philox_fill", "pc_normal_fill", "pc_seam_index_map"]
+           "pc_seam_mean_abs", "pc_mds_recover", "pc_kabsch_stitch", "pc_kabsch_stitch_proper", "pc_set_max_dispatch_items", "pc_philox_block", "pc_philox_fill", "pc_normal_fill", "pc_seam_index_map"]
 
 BEADS = 64
 PACKED = 2016
@@ -198,16 +198,25 @@ def pc_mds_recover(maps, coords, eigvals=None, max_iters: int = 0) -> None:
            "pc_mds_recover")
 
 
-def pc_kabsch_stitch(coords, layout: PCLayout, chain, residual) -> None:
+def _stitch(name: str, coords, layout: PCLayout, chain, residual) -> None:
     t = _torch()
     lay = layout.c()
     n_chains = layout.n_regions // layout.chain_len
     n_beads = (layout.chain_len - 1) * (BEADS - layout.overlap) + BEADS
-    _check(_lib.load().pc_kabsch_stitch(
+    _check(getattr(_lib.load(), name)(
         _dev(coords, t.float32, layout.n_maps * BEADS * 3, "coords"), ctypes.byref(lay),
         _dev(chain, t.float32, n_chains * layout.n_guidance * layout.n_traj * n_beads * 3, "chain"),
         _dev(residual, t.float32, layout.n_seams * layout.n_guidance * layout.n_traj, "residual"),
-        _stream(coords)), "pc_kabsch_stitch")
+        _stream(coords)), name)
+
+
+def pc_kabsch_stitch(coords, layout: PCLayout, chain, residual) -> None:
+    _stitch("pc_kabsch_stitch", coords, layout, chain, residual)
+
+
+def pc_kabsch_stitch_proper(coords, layout: PCLayout, chain, residual) -> None:
+    """pc_kabsch_stitch with every fit restricted to rotations (det +1)."""
+    _stitch("pc_kabsch_stitch_proper", coords, layout, chain, residual)
 
 
 def pc_set_max_dispatch_items(items: int) -> None:

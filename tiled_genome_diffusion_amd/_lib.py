@@ -45,6 +45,7 @@ SIGNATURES = {
     "pc_seam_mean_abs": (ctypes.c_int32, [vp, ctypes.POINTER(Layout), vp, vp]),
     "pc_mds_recover": (ctypes.c_int32, [vp, ctypes.c_int64, vp, vp, ctypes.c_int32, vp]),
     "pc_kabsch_stitch": (ctypes.c_int32, [vp, ctypes.POINTER(Layout), vp, vp, vp]),
+    "pc_kabsch_stitch_proper": (ctypes.c_int32, [vp, ctypes.POINTER(Layout), vp, vp, vp]),
     "pc_set_max_dispatch_items": (ctypes.c_int32, [ctypes.c_uint64]),
     "pc_philox_block": (ctypes.c_int32, [c_u32_p, c_u32_p, ctypes.c_uint64]),
     "pc_philox_fill": (ctypes.c_int32, [vp, ctypes.POINTER(Layout), ctypes.c_uint64, ctypes.c_uint32, vp]),

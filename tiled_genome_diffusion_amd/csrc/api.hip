@@ -355,8 +355,13 @@ pc_status pc_mds_recover(const float *maps, int64_t n_maps, float *coords, float
                       "mds launch");
 }
 
-pc_status pc_kabsch_stitch(const float *coords, const pc_layout *layout, float *chain, float *residual,
-                           void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by both stitching entry points: proper restricts the fits to rotations.
+pc_status stitch(const float *coords, const pc_layout *layout, float *chain, float *residual, bool proper,
+                 void *stream) {
     if (!coords || !chain || !residual) return fail(PC_ERR_NULL, "coords, chain and residual are required");
     int64_t n = 0;
     const pc_status st = check_layout(layout, &n);
@@ -368,9 +373,23 @@ pc_status pc_kabsch_stitch(const float *coords, const pc_layout *layout, float *
     if (!aligned16(coords) || !aligned16(chain) || !aligned16(residual))
         return fail(PC_ERR_ALIGN, "device arrays must be 16-byte aligned");
     return hip_status(pc::launch_stitch(coords, layout->n_regions / layout->chain_len, layout->n_guidance,
-                                        layout->n_traj, chain_args(layout), chain, residual,
+                                        layout->n_traj, chain_args(layout), chain, residual, proper,
                                         static_cast<hipStream_t>(stream)),
                       "stitch launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+pc_status pc_kabsch_stitch(const float *coords, const pc_layout *layout, float *chain, float *residual,
+                           void *stream) {
+    return stitch(coords, layout, chain, residual, false, stream);
+}
+
+pc_status pc_kabsch_stitch_proper(const float *coords, const pc_layout *layout, float *chain, float *residual,
+                                  void *stream) {
+    return stitch(coords, layout, chain, residual, true, stream);
 }
 
 pc_status pc_philox_block(uint32_t out[4], const uint32_t ctr[4], uint64_t seed) {

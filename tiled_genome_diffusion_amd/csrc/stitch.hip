@@ -20,6 +20,11 @@
 //   3. the wavefronts move their tiles' beads into the chain frame, one lane
 //      per bead; a shared bead takes the mean of its two aligned positions
 //      (written by the later tile).
+// PROPER restricts every fit to rotations (det +1), Kabsch's fit with the
+// determinant correction: where the polar factor Q of H is a reflection, the
+// best rotation is Q (I - 2 v v^T), v the unit eigenvector of the symmetric
+// factor P = Q^T H for its smallest eigenvalue (with H = U S V^T, Q = U V^T,
+// P = V S V^T, and the fit U diag(1, 1, -1) V^T = Q - 2 (Q v) v^T).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -79,6 +84,76 @@ __device__ __forceinline__ void polar3(float (&x)[3][3]) {
     }
 }
 
+// Unit eigenvector of a symmetric 3x3 for its smallest eigenvalue: the
+// eigenvalue from the trigonometric solution of the characteristic cubic
+// (Smith, CACM 4(4), 1961), the vector as the longest cross product of two
+// rows of P - lambda I (which spans the eigenvalue's null space).
+__device__ __forceinline__ void smallest_eigvec3(const float (&p)[3][3], float (&v)[3]) {
+    const float q = (p[0][0] + p[1][1] + p[2][2]) * (1.f / 3.f);
+    const float off = fmaf(p[0][1], p[0][1], fmaf(p[0][2], p[0][2], p[1][2] * p[1][2]));
+    const float d0 = p[0][0] - q, d1 = p[1][1] - q, d2 = p[2][2] - q;
+    const float s = sqrtf(fmaf(d0, d0, fmaf(d1, d1, fmaf(d2, d2, 2.f * off))) * (1.f / 6.f));
+    float lam = q;
+    if (s > 0.f) {
+        const float is = 1.f / s;
+        const float b[3][3] = {{d0 * is, p[0][1] * is, p[0][2] * is},
+                               {p[1][0] * is, d1 * is, p[1][2] * is},
+                               {p[2][0] * is, p[2][1] * is, d2 * is}};
+        const float r = fminf(1.f, fmaxf(-1.f, 0.5f * det3(b)));
+        lam = fmaf(2.f * s, cosf(acosf(r) * (1.f / 3.f) + 2.09439510239319549f), q);  // + 2 pi / 3
+    }
+    const float m[3][3] = {{p[0][0] - lam, p[0][1], p[0][2]},
+                           {p[1][0], p[1][1] - lam, p[1][2]},
+                           {p[2][0], p[2][1], p[2][2] - lam}};
+    float best = -1.f;
+    v[0] = 0.f;
+    v[1] = 0.f;
+    v[2] = 1.f;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b2 = a + 1; b2 < 3; ++b2) {
+            const float c[3] = {m[a][1] * m[b2][2] - m[a][2] * m[b2][1], m[a][2] * m[b2][0] - m[a][0] * m[b2][2],
+                                m[a][0] * m[b2][1] - m[a][1] * m[b2][0]};
+            const float n2 = fmaf(c[0], c[0], fmaf(c[1], c[1], c[2] * c[2]));
+            if (n2 > best) {
+                best = n2;
+                v[0] = c[0];
+                v[1] = c[1];
+                v[2] = c[2];
+            }
+        }
+    if (best > 0.f) {
+        const float in = 1.f / sqrtf(best);
+        v[0] *= in;
+        v[1] *= in;
+        v[2] *= in;
+    }
+}
+
+// q <- the best rotation for H where the polar factor q of H is a reflection.
+__device__ __forceinline__ void make_proper(float (&q)[3][3], const float (&h)[3][3]) {
+    if (!(det3(q) < 0.f)) return;
+    float pm[3][3];
+#pragma unroll
+    for (int a = 0; a < 3; ++a)
+#pragma unroll
+        for (int b = 0; b < 3; ++b) pm[a][b] = fmaf(q[0][a], h[0][b], fmaf(q[1][a], h[1][b], q[2][a] * h[2][b]));
+#pragma unroll
+    for (int a = 0; a < 3; ++a)
+#pragma unroll
+        for (int b = a + 1; b < 3; ++b) pm[a][b] = pm[b][a] = 0.5f * (pm[a][b] + pm[b][a]);
+    float v[3];
+    smallest_eigvec3(pm, v);
+    float qv[3];
+#pragma unroll
+    for (int a = 0; a < 3; ++a) qv[a] = fmaf(q[a][0], v[0], fmaf(q[a][1], v[1], q[a][2] * v[2]));
+#pragma unroll
+    for (int a = 0; a < 3; ++a)
+#pragma unroll
+        for (int b = 0; b < 3; ++b) q[a][b] = fmaf(-2.f * qv[a], v[b], q[a][b]);
+}
+
 // Rigid transform x -> x M + u of a row vector; M row-major at t[0..8], u at t[9..11].
 __device__ __forceinline__ void apply(const float *t, const float (&x)[3], float (&y)[3]) {
 #pragma unroll
@@ -107,6 +182,7 @@ __device__ __forceinline__ void identity(float (&t)[12]) {
 // y ~ x R + shift; returns the mean squared distance after the fit.  The sums
 // are shifted by each block's first bead, so centring loses nothing to
 // cancellation.
+template <bool PROPER>
 __device__ float fit(const float *x, const float *y, int O, float (&t)[12]) {
     float x0[3], y0[3], sx[3] = {0.f, 0.f, 0.f}, sy[3] = {0.f, 0.f, 0.f}, h[3][3] = {};
 #pragma unroll
@@ -139,7 +215,13 @@ __device__ float fit(const float *x, const float *y, int O, float (&t)[12]) {
     for (int a = 0; a < 3; ++a)
 #pragma unroll
         for (int b = 0; b < 3; ++b) h[a][b] = fmaf(-static_cast<float>(O) * xm[a], ym[b], h[a][b]);
+    float hc[3][3];
+#pragma unroll
+    for (int a = 0; a < 3; ++a)
+#pragma unroll
+        for (int b = 0; b < 3; ++b) hc[a][b] = h[a][b];
     polar3(h);
+    if (PROPER) make_proper(h, hc);
 #pragma unroll
     for (int a = 0; a < 3; ++a) {
         xm[a] += x0[a];
@@ -165,6 +247,7 @@ __device__ float fit(const float *x, const float *y, int O, float (&t)[12]) {
     return r2 * inv;
 }
 
+template <bool PROPER>
 __global__ __launch_bounds__(kStitchThreads) void k_stitch(const float *__restrict__ coords, int32_t G, int32_t S,
                                                            ChainArgs ch, float *__restrict__ chain,
                                                            float *__restrict__ resid, int64_t block0) {
@@ -188,7 +271,7 @@ __global__ __launch_bounds__(kStitchThreads) void k_stitch(const float *__restri
         float t[12];
         identity(t);
         if (k >= 1 && k < L) {
-            const float r2 = fit(tile(k), tile(k - 1) + stride * 3, O, t);
+            const float r2 = fit<PROPER>(tile(k), tile(k - 1) + stride * 3, O, t);
             resid[(static_cast<size_t>(c) * (L - 1) + k - 1) * n_cols + gs] = sqrtf(r2);
         }
         // inclusive scan: t_k <- t_{k-d} o t_k
@@ -268,13 +351,17 @@ __global__ __launch_bounds__(kStitchThreads) void k_stitch(const float *__restri
 }  // namespace
 
 hipError_t launch_stitch(const float *coords, int32_t n_chains, int32_t G, int32_t S, ChainArgs ch, float *chain,
-                         float *resid, hipStream_t stream) {
+                         float *resid, bool proper, hipStream_t stream) {
     if (ch.chain_len > 64 * kStitchMaxChunks) return hipErrorInvalidValue;
     const int64_t blocks = static_cast<int64_t>(n_chains) * G * S;
     const size_t lds = static_cast<size_t>(ch.chain_len + kStitchMaxChunks) * 12 * sizeof(float);
     return launch_slices(blocks, kStitchThreads, [&](int64_t first, uint32_t count) {
-        hipLaunchKernelGGL(k_stitch, dim3(count), dim3(kStitchThreads), lds, stream, coords, G, S, ch, chain, resid,
-                           first);
+        if (proper)
+            hipLaunchKernelGGL(k_stitch<true>, dim3(count), dim3(kStitchThreads), lds, stream, coords, G, S, ch, chain,
+                               resid, first);
+        else
+            hipLaunchKernelGGL(k_stitch<false>, dim3(count), dim3(kStitchThreads), lds, stream, coords, G, S, ch,
+                               chain, resid, first);
     });
 }
 
