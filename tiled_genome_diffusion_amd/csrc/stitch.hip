@@ -123,6 +123,28 @@ __device__ __forceinline__ void smallest_eigvec3(const float (&p)[3][3], float (
                 v[2] = c[2];
             }
         }
+    // Rank one or zero (the smallest eigenvalue is repeated): every vector orthogonal to the
+    // rows is an eigenvector; take one orthogonal to the longest row (any vector if all vanish).
+    float w[3] = {m[0][0], m[0][1], m[0][2]}, wn = fmaf(w[0], w[0], fmaf(w[1], w[1], w[2] * w[2]));
+#pragma unroll
+    for (int a = 1; a < 3; ++a) {
+        const float n = fmaf(m[a][0], m[a][0], fmaf(m[a][1], m[a][1], m[a][2] * m[a][2]));
+        if (n > wn) {
+            wn = n;
+            w[0] = m[a][0];
+            w[1] = m[a][1];
+            w[2] = m[a][2];
+        }
+    }
+    if (!(best > 1e-8f * wn * wn) && wn > 0.f) {
+        // w x e_j for the axis e_j least aligned with w
+        const int j = fabsf(w[0]) <= fabsf(w[1]) ? (fabsf(w[0]) <= fabsf(w[2]) ? 0 : 2)
+                                                 : (fabsf(w[1]) <= fabsf(w[2]) ? 1 : 2);
+        v[0] = j == 0 ? 0.f : (j == 1 ? -w[2] : w[1]);
+        v[1] = j == 0 ? w[2] : (j == 1 ? 0.f : -w[0]);
+        v[2] = j == 0 ? -w[1] : (j == 1 ? w[0] : 0.f);
+        best = fmaf(v[0], v[0], fmaf(v[1], v[1], v[2] * v[2]));
+    }
     if (best > 0.f) {
         const float in = 1.f / sqrtf(best);
         v[0] *= in;
