@@ -270,6 +270,9 @@ void geometry(const pc_layout &L, uint64_t cap) {
     const int64_t NP = L.overlap * (L.overlap - 1) / 2;
     stub::reset();
     CHECK(pc_ddim_cfg_step(F, F, F2, w, &L, 0.3, 0.5, 1.0, 1, 2, 1, F2, nullptr) == PC_OK);
+    EXPECT_GRIDS("k_step_chain", R * G * ceil_div(S, 8), 512, 1, cap);  // with the discrepancy: 8 maps each
+    stub::reset();
+    CHECK(pc_ddim_cfg_step(F, F, F2, w, &L, 0.3, 0.5, 1.0, 1, 2, 1, nullptr, nullptr) == PC_OK);
     EXPECT_GRIDS("k_step_chain", R * G * ceil_div(S, 6), 512, 1, cap);
 
     stub::reset();

@@ -11,6 +11,9 @@ constexpr int kChainU = 1;           // maps per lane per barrier, chain layout 
 // clocks: 6 is best for both the 16,384-map and the 32,000-map chain (41.8 and
 // 76.2 us per step; 8 maps: 41.8 and 78.8; 4: 44 and 80; 10: 44.8 and 80.6).
 constexpr int kChainMaps = 6;
+// With the pre-projection discrepancy output, 8 (measured: 46.9 and 85.1 us against 48.2 and
+// 87.1 with 6; 10 and 12 maps: 50.0 / 84.7 and 49.6 / 84.9).
+constexpr int kChainMapsDisc = 8;
 // The wavefront that sums the pre-projection discrepancy: the last one, which
 // holds the right-seam lines and the idle lanes past the map's 504 quads.
 constexpr uint32_t kDiscWave = kThreads / 64 - 1;
@@ -203,10 +206,10 @@ hipError_t launch_step_chain(float *state, const float *x0c, const float *x0u, c
                              StepArgs a, ChainArgs ch, bool project, float *pre_disc, bool noise, bool init,
                              hipStream_t stream) {
     const int64_t n_maps = static_cast<int64_t>(a.R) * a.G * a.S;
-    a.maps_per_block = kChainMaps;
+    const bool disc = pre_disc != nullptr;
+    a.maps_per_block = disc ? kChainMapsDisc : kChainMaps;
     a.blocks_per_rg = (a.S + a.maps_per_block - 1) / a.maps_per_block;
     const int64_t blocks = static_cast<int64_t>(a.R) * a.G * a.blocks_per_rg;
-    const bool disc = pre_disc != nullptr;
     const bool nt = static_cast<size_t>(n_maps) * kPacked * 4 > kStreamBytes;
     const bool eps = eps_c != nullptr;
     return launch_slices(blocks, kThreads, [&](int64_t first, uint32_t count) {
