@@ -86,6 +86,10 @@ def parse():
                    help="on a chain workload: per-step seam discrepancy before projection (the fused "
                         "discrepancy output of the step) and after it (pc_seam_discrepancy), against the "
                         "closed-form expectation, and the step time with and without the discrepancy output")
+    p.add_argument("--mds-inputs", action="store_true",
+                   help="time MDS alone over the workload's map count on three kinds of input: the exact "
+                        "final maps, the same with 1e-3 relative noise, and equal mixtures of two regions' maps "
+                        "(not Euclidean); one JSON line")
     p.add_argument("--jacobi-maps", type=int, default=8,
                    help="maps the cpu baseline runs through the Jacobi MDS oracle (0.5 s each on one core)")
     return p.parse_args()
@@ -416,6 +420,49 @@ def sync_ablation(args, wl, n_steps):
                               "discrepancy and drift do not depend on K"}), flush=True)
 
 
+def mds_inputs(args, wl):
+    """pc_mds_recover on inputs of three kinds, each as many maps as the workload holds, laid out
+    like its final state ([R][G][S], map (r, g, s) = the reference that weight g lands on): exact
+    maps, maps with seeded 1e-3 relative Gaussian noise (torch's generator on the device), and
+    equal mixtures of region r's and region r+1's maps.  HIP events around back-to-back launches
+    (median of args.steps, after three untimed ones)."""
+    import numpy as np
+    import torch
+
+    import tiled_genome_diffusion_amd as pc
+    from workloads import reference_maps
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    x0c, x0u = reference_maps(wl, args.seed)
+    xc, xu = torch.from_numpy(x0c).to(dev), torch.from_numpy(x0u).to(dev)
+    w = torch.tensor(list(wl.w), dtype=torch.float32, device=dev)
+    per_rg = (xu[:, None, :] + w[None, :, None] * (xc - xu)[:, None, :])  # [R][G][2016], fp32
+    exact = per_rg[:, :, None, :].expand(wl.n_regions, wl.n_guidance, wl.n_traj, 2016).reshape(-1, 2016).contiguous()
+    gen = torch.Generator(device=dev).manual_seed(args.seed)
+    noisy = exact * (1.0 + 1e-3 * torch.randn(exact.shape, generator=gen, device=dev))
+    mixed = 0.5 * (exact + torch.roll(exact, shifts=wl.n_guidance * wl.n_traj, dims=0))
+    n = exact.shape[0]
+    coords = torch.empty(n * 192, dtype=torch.float32, device=dev)
+    rows = {}
+    for name, maps in (("exact", exact), ("noisy_1e-3", noisy), ("two_map_mixture", mixed)):
+        flat = maps.reshape(-1)
+        for _ in range(3):
+            pc.pc_mds_recover(flat, coords)
+        times = []
+        for _ in range(max(1, args.steps)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            pc.pc_mds_recover(flat, coords)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ms = float(np.median(times))
+        gbs = MDS_BYTES_PER_MAP * n / (ms * 1e-3) / 1e9
+        rows[name] = {"ms": ms, "maps_per_s": n / (ms * 1e-3), "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+    print(json.dumps({"metric": "MDS by input kind", "workload": wl.name, "maps": n, "rows": rows}), flush=True)
+
+
 def chain_kernels(args, wl, n_steps):
     """Per-call times of the chain kernels that sit beside the step loop, on the final state
     and MDS coordinates of one projected pass: HIP events around repeated calls on one stream,
@@ -630,6 +677,8 @@ def main():
         return ceilings(args, wl)
     if args.seam_report:
         return seam_report(args, wl, n_steps)
+    if args.mds_inputs:
+        return mds_inputs(args, wl)
     dev = torch.device("cuda:0")
     lay = pc.PCLayout(wl.n_regions, wl.n_guidance, wl.n_traj, wl.chain_len, wl.overlap if wl.chain_len > 1 else 0)
     seeds = [int(v) for v in args.seeds.split(",")]
