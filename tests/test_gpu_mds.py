@@ -156,3 +156,20 @@ def test_batch_slices_match_the_whole_batch():
         out = torch.empty((hi - lo) * 64 * 3, dtype=torch.float32, device=dev)
         pc.pc_mds_recover(maps[lo:hi], out)
         assert torch.equal(out.view(hi - lo, 64, 3), whole[lo:hi])
+
+
+def test_scaling_the_distances_by_four_scales_the_output_exactly():
+    """Every test and threshold of the kernel is relative, so distances times 4 (exact in
+    float32) give coordinates times 4 and eigenvalues times 16, bit for bit: on exact walk
+    maps, noisy ones and maps that are not Euclidean."""
+    say("mds: scale equivariance")
+    rng = np.random.default_rng(17)
+    walks = [random_walk(64, walk_rng(19, k), None) for k in range(24)]
+    exact = np.array([packed_distances(w) for w in walks], dtype=np.float32)
+    noisy = (exact * (1.0 + 1e-3 * rng.standard_normal(exact.shape))).astype(np.float32)
+    mixed = (0.5 * (exact + np.roll(exact, 1, axis=0))).astype(np.float32)
+    maps = np.concatenate([exact, noisy, mixed])
+    c1, e1 = gpu_mds(maps)
+    c4, e4 = gpu_mds(maps * np.float32(4.0))
+    assert np.array_equal(c4, c1 * np.float32(4.0))
+    assert np.array_equal(e4, e1 * np.float32(16.0))

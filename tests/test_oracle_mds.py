@@ -106,3 +106,21 @@ def test_procrustes_undoes_rotation_reflection_translation():
     assert resid < 1e-12 and np.allclose(aligned, y, atol=1e-12)
     _, resid = mds.procrustes(x + rng.standard_normal(x.shape) * 0.1, y)
     assert resid > 0.01
+
+
+def test_equivariance_under_scaling_and_bead_relabelling():
+    """Distances scaled by c give coordinates scaled by c and eigenvalues by c^2; relabelling the
+    beads relabels the coordinates (the sign convention follows the entries, not their index,
+    wherever the largest magnitude is unique)."""
+    rng = np.random.default_rng(3)
+    for k in range(4):
+        walk = random_walk(64, walk_rng(11, k), None)
+        d = packed_distances(walk)
+        x, lam = mds.classical_mds(d)
+        xs, lams = mds.classical_mds(3.0 * d)
+        assert np.allclose(xs, 3.0 * x, atol=1e-9 * np.abs(x).max())
+        assert np.allclose(lams, 9.0 * lam, rtol=1e-12)
+        perm = rng.permutation(64)
+        xp, lamp = mds.classical_mds(packed_distances(walk[perm]))
+        assert np.allclose(lamp, lam, rtol=1e-12)
+        assert np.allclose(xp, x[perm], atol=1e-9 * np.abs(x).max())
